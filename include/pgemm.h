@@ -1,0 +1,150 @@
+/*
+ * libpgemm -- software-pipelined tiled fp16 GEMM and streaming elementwise
+ * kernels for AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * Plain C ABI: raw pointers, 64-bit sizes, an opaque stream handle.  Device
+ * pointers are HIP device addresses (for example torch tensor data_ptr()).
+ * The stream argument is a hipStream_t passed as void*; NULL selects the
+ * default (null) stream.
+ *
+ * Common contract for every compute entry point:
+ *  - Arguments are validated on the host before any HIP call.  A rejected
+ *    call returns a negative status and touches no memory.
+ *  - Work is enqueued asynchronously on `stream`; the call never
+ *    synchronises, never allocates device memory and keeps no pointer after
+ *    it returns.  The caller keeps the buffers alive until the stream has
+ *    executed the work.
+ *  - Outputs are write-only: their previous contents never influence the
+ *    result (the buffer-revisiting rule of the Pallas software-pipelining
+ *    guide, section 7.1: output buffers are written, not read).
+ *  - PGEMM_EHIP means the kernel launch itself failed; pgemm_last_hip_error()
+ *    then returns the hipError_t value (as int) for the calling thread.
+ *    Errors of kernels that already ran asynchronously are reported by the
+ *    stream, not by this library.
+ */
+#ifndef PGEMM_H
+#define PGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* pgemm_stream_t; /* a hipStream_t */
+
+enum pgemm_status {
+    PGEMM_OK = 0,
+    PGEMM_EINVAL = -1,       /* null pointer with a non-zero size, negative size, overlap */
+    PGEMM_EUNSUPPORTED = -2, /* valid request outside what the kernels handle */
+    PGEMM_EHIP = -3          /* the HIP launch failed */
+};
+
+/*
+ * C[M,N] = A[M,K] . B[K,N]
+ *
+ * The matmul of the Pallas "Quickstart: GPU" page, section "Pipelining: a
+ * matmul kernel" (and section "Hopper 上的矩阵乘法内核" of its Chinese
+ * rewrite): a parallel grid of output tiles, one workgroup per tile, and a
+ * sequential loop over K whose global->LDS copies for later steps are in
+ * flight while the matrix cores work on the current step.
+ *
+ * A, B, C: IEEE binary16, dense row-major, no leading-dimension arguments
+ * (A is M x K with K contiguous, B is K x N with N contiguous, C is M x N).
+ * Products are accumulated in fp32; each output is rounded once to binary16,
+ * round-to-nearest-even (infinities on overflow, subnormals kept).  The
+ * summation order inside fp32 is unspecified but fixed: identical inputs give
+ * bit-identical outputs, call after call.
+ *
+ * Requirements: M, N, K >= 0; K % 8 == 0 and N % 8 == 0 (rows are moved in
+ * 16-byte pieces); A, B, C 16-byte aligned; K < 2^22 and N < 2^23; the C
+ * range must not overlap A or B.
+ *   M == 0 or N == 0: PGEMM_OK, nothing is enqueued.
+ *   K == 0: C is filled with +0.0 (the empty sum).
+ * Rows and columns that do not fill a whole tile are handled (no
+ * truncation).
+ * Returns PGEMM_EINVAL (null pointer with non-zero extent, negative size,
+ * overlap of C with A or B), PGEMM_EUNSUPPORTED (alignment or divisibility
+ * not met, sizes beyond the limits), PGEMM_EHIP, or PGEMM_OK.
+ */
+int pgemm_f16(const void* A, const void* B, void* C,
+              int64_t M, int64_t N, int64_t K, pgemm_stream_t stream);
+
+/*
+ * Same as pgemm_f16 with the tile configuration forced (tests and
+ * benchmarks).  `variant`:
+ *   0  automatic choice (what pgemm_f16 does)
+ *   1  256x256 output tile per workgroup, 64-deep K steps, 4 waves
+ *   2  128x128 output tile per workgroup, 64-deep K steps, 4 waves (the
+ *      128x128x64 tiling of the quickstart's matmul)
+ * Every variant gives bit-identical results for the same inputs (the K
+ * order inside each output element does not depend on the tiling).
+ * Unknown variants return PGEMM_EUNSUPPORTED.
+ */
+int pgemm_f16_variant(const void* A, const void* B, void* C,
+                      int64_t M, int64_t N, int64_t K, int variant,
+                      pgemm_stream_t stream);
+
+/* Number of GEMM variants accepted by pgemm_f16_variant (largest id). */
+int pgemm_f16_num_variants(void);
+
+/*
+ * z[i] = x[i] + y[i], i in [0, n): one IEEE binary32 addition per element,
+ * round-to-nearest-even, no flush to zero -- bit-identical to any IEEE
+ * implementation.  The pipelined elementwise add of the Pallas
+ * software-pipelining guide, section 6 (copy_in / compute / copy_out per
+ * block, neighbouring blocks overlapped); the data goes global -> registers
+ * -> global without LDS (quickstart, section "GPU memory spaces": ALU work
+ * bypasses shared memory).
+ * x, y, z: device float arrays of n elements.  z may be exactly x or exactly
+ * y (in place); any other overlap returns PGEMM_EINVAL.  n == 0 enqueues
+ * nothing.  Any alignment is accepted (16-byte aligned arrays take the
+ * vector path).
+ */
+int pstream_add(const float* x, const float* y, float* z, int64_t n,
+                pgemm_stream_t stream);
+
+/*
+ * pstream_add with the per-workgroup block size forced: each workgroup
+ * copies in, adds and copies out one contiguous block of `block_elems`
+ * elements (the block-size parameter of the guide's section 6.1; 512*512 by
+ * default).  block_elems must be a positive multiple of 1024 and at most
+ * 2^24, else PGEMM_EUNSUPPORTED.  Results do not depend on it.
+ */
+int pstream_add_blocked(const float* x, const float* y, float* z, int64_t n,
+                        int64_t block_elems, pgemm_stream_t stream);
+
+/*
+ * z[i] = x[i] + c: the "+1" loop of the software-pipelining guide,
+ * section 4, which writes its result back over its input (z == x is
+ * allowed; any other overlap returns PGEMM_EINVAL).  One binary32 addition
+ * per element.  Reads one array, so it moves 8 bytes per element.
+ */
+int pstream_add_scalar(const float* x, float c, float* z, int64_t n,
+                       pgemm_stream_t stream);
+
+/*
+ * Worked examples of the quickstart, exported for tests:
+ *  pgemm_test_fill_f32: o[i] = v for i in [0, n) ("Your first kernel":
+ *    128 elements of 42.0).
+ *  pgemm_test_iota_f32: o[i] = (float)i, rounded to nearest-even ("Parallel
+ *    work with a grid": 8 blocks of 128, block b writes its own slice).
+ * n == 0 enqueues nothing; o == NULL with n > 0 returns PGEMM_EINVAL.
+ */
+int pgemm_test_fill_f32(float* o, float v, int64_t n, pgemm_stream_t stream);
+int pgemm_test_iota_f32(float* o, int64_t n, pgemm_stream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char* pgemm_status_string(int status);
+
+/* hipError_t of the last PGEMM_EHIP on the calling thread (0 if none). */
+int pgemm_last_hip_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int pgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PGEMM_H */

@@ -1,0 +1,151 @@
+"""libpgemm for MI355X (gfx950): software-pipelined tiled fp16 GEMM and the
+pipelined streaming elementwise add, behind a plain C ABI (include/pgemm.h).
+
+The functions below carry the C ABI's names and take torch tensors; they only
+check arguments, pick the stream and pass pointers.  torch supplies device
+memory and streams; all arithmetic happens in the HIP kernels.  Loading is
+lazy (importing the package does not touch the GPU or the library), and a
+missing library raises -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+from ._lib import (PGEMM_EHIP, PGEMM_EINVAL, PGEMM_EUNSUPPORTED, PGEMM_OK, PgemmError,
+                   lib, status_string)
+
+__all__ = [
+    "pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants",
+    "pstream_add", "pstream_add_blocked", "pstream_add_scalar",
+    "pgemm_test_fill_f32", "pgemm_test_iota_f32",
+    "lib", "status_string", "PgemmError",
+    "PGEMM_OK", "PGEMM_EINVAL", "PGEMM_EUNSUPPORTED", "PGEMM_EHIP",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(device, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def _check_dev(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device (HIP) tensor, got %s" % (name, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions" % (name, ndim))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (row-major)" % name)
+
+
+def _call(rc, what):
+    if rc != PGEMM_OK:
+        raise PgemmError(rc, what)
+
+
+def pgemm_f16(A, B, C=None, stream=None):
+    """C = A @ B for fp16 row-major A [M,K], B [K,N]; returns C [M,N] fp16."""
+    return pgemm_f16_variant(A, B, 0, C=C, stream=stream)
+
+
+def pgemm_f16_variant(A, B, variant, C=None, stream=None):
+    """pgemm_f16 with the tile configuration forced (0 = automatic)."""
+    torch = _torch()
+    _check_dev(A, torch.float16, "A", 2)
+    _check_dev(B, torch.float16, "B", 2)
+    if A.device != B.device:
+        raise ValueError("A and B are on different devices")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ: %s @ %s" % (tuple(A.shape), tuple(B.shape)))
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    else:
+        _check_dev(C, torch.float16, "C", 2)
+        if tuple(C.shape) != (M, N) or C.device != A.device:
+            raise ValueError("C must be a (%d, %d) tensor on %s" % (M, N, A.device))
+    with torch.cuda.device(A.device):
+        rc = lib().pgemm_f16_variant(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K,
+                                     int(variant), _stream_handle(A.device, stream))
+    _call(rc, "pgemm_f16")
+    return C
+
+
+def pgemm_f16_num_variants():
+    return lib().pgemm_f16_num_variants()
+
+
+def _elementwise_out(x, z):
+    torch = _torch()
+    if z is None:
+        return torch.empty_like(x)
+    _check_dev(z, torch.float32, "z")
+    if z.numel() != x.numel() or z.device != x.device:
+        raise ValueError("z must have x's size and device")
+    return z
+
+
+def pstream_add(x, y, z=None, stream=None):
+    """z = x + y elementwise (fp32, bit-exact IEEE); z may be x or y."""
+    return pstream_add_blocked(x, y, None, z=z, stream=stream)
+
+
+def pstream_add_blocked(x, y, block_elems, z=None, stream=None):
+    """pstream_add with the per-workgroup block size forced (None = default)."""
+    torch = _torch()
+    _check_dev(x, torch.float32, "x")
+    _check_dev(y, torch.float32, "y")
+    if x.numel() != y.numel() or x.device != y.device:
+        raise ValueError("x and y must have the same size and device")
+    z = _elementwise_out(x, z)
+    with torch.cuda.device(x.device):
+        h = _stream_handle(x.device, stream)
+        if block_elems is None:
+            rc = lib().pstream_add(x.data_ptr(), y.data_ptr(), z.data_ptr(), x.numel(), h)
+        else:
+            rc = lib().pstream_add_blocked(x.data_ptr(), y.data_ptr(), z.data_ptr(), x.numel(),
+                                           int(block_elems), h)
+    _call(rc, "pstream_add")
+    return z
+
+
+def pstream_add_scalar(x, c, z=None, stream=None):
+    """z = x + c elementwise (fp32); z may be x (in place)."""
+    torch = _torch()
+    _check_dev(x, torch.float32, "x")
+    z = _elementwise_out(x, z)
+    with torch.cuda.device(x.device):
+        rc = lib().pstream_add_scalar(x.data_ptr(), float(c), z.data_ptr(), x.numel(),
+                                      _stream_handle(x.device, stream))
+    _call(rc, "pstream_add_scalar")
+    return z
+
+
+def pgemm_test_fill_f32(n, v=42.0, device="cuda", out=None, stream=None):
+    torch = _torch()
+    o = out if out is not None else torch.empty(int(n), dtype=torch.float32, device=device)
+    _check_dev(o, torch.float32, "out")
+    with torch.cuda.device(o.device):
+        rc = lib().pgemm_test_fill_f32(o.data_ptr(), float(v), o.numel(),
+                                       _stream_handle(o.device, stream))
+    _call(rc, "pgemm_test_fill_f32")
+    return o
+
+
+def pgemm_test_iota_f32(n, device="cuda", out=None, stream=None):
+    torch = _torch()
+    o = out if out is not None else torch.empty(int(n), dtype=torch.float32, device=device)
+    _check_dev(o, torch.float32, "out")
+    with torch.cuda.device(o.device):
+        rc = lib().pgemm_test_iota_f32(o.data_ptr(), o.numel(), _stream_handle(o.device, stream))
+    _call(rc, "pgemm_test_iota_f32")
+    return o

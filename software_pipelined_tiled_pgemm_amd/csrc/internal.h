@@ -1,0 +1,33 @@
+// Internal launch interface between the C ABI (pgemm_api.hip) and the
+// kernels.  Arguments reaching these functions have been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pgemm {
+
+// GEMM tile configurations (ids match pgemm_f16_variant).
+enum GemmVariant : int {
+    kGemmAuto = 0,
+    kGemm256x256 = 1,
+    kGemm128x128 = 2,
+    kGemmNumVariants = 2,
+};
+
+// Picks a concrete variant for a problem shape.
+int gemm_choose_variant(int64_t M, int64_t N, int64_t K);
+
+hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                           int64_t K, int variant, hipStream_t stream);
+
+constexpr int64_t kStreamDefaultBlock = 512 * 512;  // elements per workgroup block
+
+hipError_t launch_stream_add(const float* x, const float* y, float* z, int64_t n,
+                             int64_t block_elems, hipStream_t stream);
+hipError_t launch_stream_add_scalar(const float* x, float c, float* z, int64_t n,
+                                    hipStream_t stream);
+hipError_t launch_fill(float* o, float v, int64_t n, hipStream_t stream);
+hipError_t launch_iota(float* o, int64_t n, hipStream_t stream);
+
+}  // namespace pgemm

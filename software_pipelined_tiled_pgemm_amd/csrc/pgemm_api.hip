@@ -1,0 +1,128 @@
+// C ABI of libpgemm: argument validation, status codes, dispatch.
+// Every check runs on the host before any HIP call; a rejected call touches
+// no memory and enqueues nothing.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pgemm.h"
+#include "internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return PGEMM_OK;
+    g_last_hip_error = (int)e;
+    return PGEMM_EHIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) (bytes) share at least one byte.
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    if (na <= 0 || nb <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+// Elementwise operands: either the same array or disjoint.
+bool bad_alias(const void* out, const void* in, int64_t bytes) {
+    return out != in && overlap(out, bytes, in, bytes);
+}
+
+constexpr int64_t kMaxK = (int64_t)1 << 22;
+constexpr int64_t kMaxN = (int64_t)1 << 23;
+constexpr int64_t kMaxM = ((int64_t)1 << 31) - 256;
+
+int check_gemm(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return PGEMM_EINVAL;
+    if (M == 0 || N == 0) return PGEMM_OK;
+    if (!C) return PGEMM_EINVAL;
+    if (K > 0 && (!A || !B)) return PGEMM_EINVAL;
+    if (K % 8 != 0 || N % 8 != 0) return PGEMM_EUNSUPPORTED;
+    if (K >= kMaxK || N >= kMaxN || M >= kMaxM) return PGEMM_EUNSUPPORTED;
+    if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B)))) return PGEMM_EUNSUPPORTED;
+    const int64_t cb = M * N * 2;
+    if (K > 0 && (overlap(C, cb, A, M * K * 2) || overlap(C, cb, B, K * N * 2)))
+        return PGEMM_EINVAL;
+    return PGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pgemm_f16_variant(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                      int variant, pgemm_stream_t stream) {
+    if (variant < 0 || variant > pgemm::kGemmNumVariants) return PGEMM_EUNSUPPORTED;
+    const int rc = check_gemm(A, B, C, M, N, K);
+    if (rc != PGEMM_OK) return rc;
+    if (M == 0 || N == 0) return PGEMM_OK;
+    return hip_status(pgemm::launch_gemm_f16(A, B, C, M, N, K, variant,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int pgemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+              pgemm_stream_t stream) {
+    return pgemm_f16_variant(A, B, C, M, N, K, pgemm::kGemmAuto, stream);
+}
+
+int pgemm_f16_num_variants(void) { return pgemm::kGemmNumVariants; }
+
+int pstream_add_blocked(const float* x, const float* y, float* z, int64_t n, int64_t block_elems,
+                        pgemm_stream_t stream) {
+    if (n < 0) return PGEMM_EINVAL;
+    if (block_elems <= 0 || block_elems % 1024 != 0 || block_elems > ((int64_t)1 << 24))
+        return PGEMM_EUNSUPPORTED;
+    if (n == 0) return PGEMM_OK;
+    if (!x || !y || !z) return PGEMM_EINVAL;
+    const int64_t bytes = n * (int64_t)sizeof(float);
+    if (bad_alias(z, x, bytes) || bad_alias(z, y, bytes)) return PGEMM_EINVAL;
+    if ((n + block_elems - 1) / block_elems > 0x7FFFFFFF) return PGEMM_EUNSUPPORTED;
+    return hip_status(
+        pgemm::launch_stream_add(x, y, z, n, block_elems, static_cast<hipStream_t>(stream)));
+}
+
+int pstream_add(const float* x, const float* y, float* z, int64_t n, pgemm_stream_t stream) {
+    return pstream_add_blocked(x, y, z, n, pgemm::kStreamDefaultBlock, stream);
+}
+
+int pstream_add_scalar(const float* x, float c, float* z, int64_t n, pgemm_stream_t stream) {
+    if (n < 0) return PGEMM_EINVAL;
+    if (n == 0) return PGEMM_OK;
+    if (!x || !z) return PGEMM_EINVAL;
+    if (bad_alias(z, x, n * (int64_t)sizeof(float))) return PGEMM_EINVAL;
+    return hip_status(pgemm::launch_stream_add_scalar(x, c, z, n, static_cast<hipStream_t>(stream)));
+}
+
+int pgemm_test_fill_f32(float* o, float v, int64_t n, pgemm_stream_t stream) {
+    if (n < 0) return PGEMM_EINVAL;
+    if (n == 0) return PGEMM_OK;
+    if (!o) return PGEMM_EINVAL;
+    return hip_status(pgemm::launch_fill(o, v, n, static_cast<hipStream_t>(stream)));
+}
+
+int pgemm_test_iota_f32(float* o, int64_t n, pgemm_stream_t stream) {
+    if (n < 0) return PGEMM_EINVAL;
+    if (n == 0) return PGEMM_OK;
+    if (!o) return PGEMM_EINVAL;
+    return hip_status(pgemm::launch_iota(o, n, static_cast<hipStream_t>(stream)));
+}
+
+const char* pgemm_status_string(int status) {
+    switch (status) {
+        case PGEMM_OK: return "ok";
+        case PGEMM_EINVAL: return "invalid argument (null pointer, negative size or overlapping buffers)";
+        case PGEMM_EUNSUPPORTED: return "unsupported request (alignment, divisibility, size limit or variant)";
+        case PGEMM_EHIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int pgemm_last_hip_error(void) { return g_last_hip_error; }
+
+int pgemm_version(void) { return 100; }
+
+}  // extern "C"

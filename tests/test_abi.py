@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects bad arguments on the host before any HIP
+call (so these run on a machine without a GPU)."""
+import ctypes
+import os
+
+import pytest
+
+import software_pipelined_tiled_pgemm_amd as pg
+from software_pipelined_tiled_pgemm_amd import _lib
+
+EINVAL, EUNSUP, OK = pg.PGEMM_EINVAL, pg.PGEMM_EUNSUPPORTED, pg.PGEMM_OK
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from software_pipelined_tiled_pgemm_amd import build
+        build.build()
+    return pg.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _lib.declared_functions()
+    for n in ["pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants", "pstream_add",
+              "pstream_add_blocked", "pstream_add_scalar", "pgemm_test_fill_f32",
+              "pgemm_test_iota_f32", "pgemm_status_string", "pgemm_last_hip_error",
+              "pgemm_version"]:
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _lib.declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, 7):
+        assert isinstance(pg.status_string(s), str) and pg.status_string(s)
+    assert pg.status_string(0) == "ok"
+    assert L.pgemm_last_hip_error() == 0
+    assert L.pgemm_version() >= 100
+    assert L.pgemm_f16_num_variants() >= 2
+
+
+# Fake, never dereferenced addresses (16-byte aligned, far apart).
+A, B, C = 0x10000000, 0x20000000, 0x30000000
+
+
+@pytest.mark.parametrize("args,expected", [
+    ((A, B, C, -1, 8, 8), EINVAL),
+    ((A, B, C, 8, -8, 8), EINVAL),
+    ((A, B, C, 8, 8, -8), EINVAL),
+    ((0, B, C, 8, 8, 8), EINVAL),
+    ((A, 0, C, 8, 8, 8), EINVAL),
+    ((A, B, 0, 8, 8, 8), EINVAL),
+    ((A, B, C, 8, 8, 12), EUNSUP),          # K % 8
+    ((A, B, C, 8, 12, 8), EUNSUP),          # N % 8
+    ((A + 2, B, C, 8, 8, 8), EUNSUP),       # alignment
+    ((A, B + 8, C, 8, 8, 8), EUNSUP),
+    ((A, B, C + 4, 8, 8, 8), EUNSUP),
+    ((A, B, C, 8, 8, 1 << 22), EUNSUP),     # K limit
+    ((A, B, A + 16, 8, 8, 8), EINVAL),      # C overlaps A
+    ((A, B, B, 8, 8, 8), EINVAL),           # C is B
+    ((0, 0, 0, 0, 8, 8), OK),               # empty: nothing enqueued
+    ((0, 0, 0, 8, 0, 8), OK),
+])
+def test_gemm_argument_checks(L, args, expected):
+    assert L.pgemm_f16(*args, None) == expected
+
+
+def test_gemm_variant_range(L):
+    assert L.pgemm_f16_variant(A, B, C, 8, 8, 8, -1, None) == EUNSUP
+    assert L.pgemm_f16_variant(A, B, C, 8, 8, 8, L.pgemm_f16_num_variants() + 1, None) == EUNSUP
+
+
+@pytest.mark.parametrize("x,y,z,n,expected", [
+    (A, B, C, -1, EINVAL),
+    (0, B, C, 4, EINVAL),
+    (A, 0, C, 4, EINVAL),
+    (A, B, 0, 4, EINVAL),
+    (A, B, A + 4, 4, EINVAL),   # partial overlap with x
+    (A, B, B - 4, 4, EINVAL),   # partial overlap with y
+    (0, 0, 0, 0, OK),
+])
+def test_stream_add_argument_checks(L, x, y, z, n, expected):
+    assert L.pstream_add(x, y, z, n, None) == expected
+
+
+def test_stream_add_block_checks(L):
+    assert L.pstream_add_blocked(A, B, C, 16, 0, None) == EUNSUP
+    assert L.pstream_add_blocked(A, B, C, 16, 1000, None) == EUNSUP
+    assert L.pstream_add_blocked(A, B, C, 16, (1 << 24) + 1024, None) == EUNSUP
+    assert L.pstream_add_blocked(A, B, C, 0, 1024, None) == OK
+
+
+def test_scalar_and_test_kernels_argument_checks(L):
+    assert L.pstream_add_scalar(A, 1.0, A + 4, 4, None) == EINVAL
+    assert L.pstream_add_scalar(0, 1.0, C, 4, None) == EINVAL
+    assert L.pstream_add_scalar(A, 1.0, C, -2, None) == EINVAL
+    assert L.pstream_add_scalar(0, 1.0, 0, 0, None) == OK
+    assert L.pgemm_test_fill_f32(0, 1.0, 4, None) == EINVAL
+    assert L.pgemm_test_fill_f32(0, 1.0, 0, None) == OK
+    assert L.pgemm_test_iota_f32(0, 4, None) == EINVAL
+    assert L.pgemm_test_iota_f32(A, -1, None) == EINVAL
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros((8, 8), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        pg.pgemm_f16(a, a)
+    with pytest.raises(ValueError):
+        pg.pstream_add(torch.zeros(4), torch.zeros(4))
+
+
+def test_product_package_does_not_reference_the_oracle():
+    pkg = os.path.dirname(pg.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(root, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "liboracle" not in text and "oracle_" not in text, f

@@ -1,0 +1,349 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: bit-exact for the streaming add, x + c, fill and iota; for the GEMM
+|gpu - oracle| <= 5e-3 * (|oracle| + 1) per element on inputs in [-1, 1],
+bit-exact where the exact result is an fp16 value that fp32 accumulation
+reaches exactly (identity, ones, power-of-two rank-1).  Full-size GEMMs are
+checked on a deterministic sample of outputs computed one by one by the
+oracle; smaller shapes that span several tiles and a ragged edge are checked
+element by element."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import software_pipelined_tiled_pgemm_amd as pg
+from software_pipelined_tiled_pgemm_amd import inputs
+from tests import _golden
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    pg.lib()  # raises if the library is missing: no fallback
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def gemm(A, B, variant=0, C=None):
+    say("  gemm M=%d N=%d K=%d variant=%d" % (A.shape[0], B.shape[1], A.shape[1], variant))
+    tA = A if isinstance(A, torch.Tensor) else dev(A)
+    tB = B if isinstance(B, torch.Tensor) else dev(B)
+    return host(pg.pgemm_f16_variant(tA, tB, variant, C=C))
+
+
+def assert_close(got, ref, what=""):
+    g = got.astype(np.float64)
+    r = ref.astype(np.float64)
+    ok = np.abs(g - r) <= TOL * (np.abs(r) + 1.0)
+    if not ok.all():
+        idx = np.argwhere(~ok)[:8]
+        detail = ", ".join("%s: gpu %r oracle %r" % (tuple(i), g[tuple(i)], r[tuple(i)]) for i in idx)
+        pytest.fail("%s: %d of %d outside tolerance; first: %s" % (what, (~ok).sum(), ok.size, detail))
+
+
+def bits_equal(a, b):
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    return np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+VARIANTS = [1, 2]
+
+
+# ------------------------------------------------------------ worked examples
+
+def test_fill_42_matches_pages():
+    say("fill_42")
+    got = host(pg.pgemm_test_fill_f32(128, 42.0))
+    assert bits_equal(got, _golden.values_f32("fill_42.txt"))
+
+
+def test_iota_matches_pages():
+    say("iota 1024")
+    got = host(pg.pgemm_test_iota_f32(1024))
+    assert bits_equal(got, _golden.values_f32("iota_1024.txt"))
+
+
+@pytest.mark.parametrize("n", [1, 127, 129, 3_000_001, (1 << 24) + 3])
+def test_iota_large_vs_oracle(n):
+    say("iota n=%d" % n)
+    assert bits_equal(host(pg.pgemm_test_iota_f32(n)), oracle.iota_f32(n))
+
+
+def test_ones_add_512_matches_pages():
+    say("ones+ones 512x512")
+    g = _golden.keyed("ones_add_512.txt")
+    shape = tuple(int(s) for s in g["shape"])
+    x = torch.full(shape, float(g["operand"][0]), dtype=torch.float32, device="cuda:0")
+    z = host(pg.pstream_add(x, x))
+    assert np.all(z == np.float32(g["expected"][0]))
+
+
+# ------------------------------------------------------------ streaming add
+
+def test_stream_add_full_size_bit_exact():
+    say("stream add 8192x8192 uniform[-1,1]")
+    x, y = inputs.stream_inputs((8192, 8192))
+    got = host(pg.pstream_add(dev(x), dev(y)))
+    assert bits_equal(got, oracle.add_f32(x, y))
+
+
+@pytest.mark.parametrize("bm", [128, 256, 512])
+def test_stream_add_block_sizes(bm):
+    # The guide's section 6.1 checks x + y at 128, 256 and 512 blocks of a
+    # 4096 x 4096 array; here each workgroup block holds bm*bm elements.
+    say("stream add 4096x4096 block %dx%d" % (bm, bm))
+    x, y = inputs.stream_inputs((4096, 4096), 10, 11)
+    got = host(pg.pstream_add_blocked(dev(x), dev(y), bm * bm))
+    assert bits_equal(got, oracle.add_f32(x, y))
+
+
+SPECIAL = np.array([0.0, -0.0, 1.0, -1.0, 1e-45, -1e-45, 1e-40, 1.1754942e-38, 3.4028235e38,
+                    -3.4028235e38, np.inf, -np.inf, 0.5, 2.0 ** -24, 7.0], dtype=np.float32)
+
+
+def test_stream_add_special_values():
+    say("stream add special values")
+    x = np.repeat(SPECIAL, SPECIAL.size)
+    y = np.tile(SPECIAL, SPECIAL.size)
+    got = host(pg.pstream_add(dev(x), dev(y)))
+    assert bits_equal(got, oracle.add_f32(x, y))
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 1023, 1025, 262143, 262145, 1_000_003])
+def test_stream_add_ragged_lengths(n):
+    say("stream add n=%d" % n)
+    x, y = inputs.stream_inputs(n, 20, 21)
+    got = host(pg.pstream_add(dev(x), dev(y)))
+    assert bits_equal(got, oracle.add_f32(x, y))
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_stream_add_misaligned_views(offset):
+    say("stream add misaligned offset %d" % offset)
+    n = 100_000
+    x, y = inputs.stream_inputs(n + offset, 30, 31)
+    tx, ty = dev(x)[offset:], dev(y)[offset:]
+    z = torch.empty(n + offset, dtype=torch.float32, device="cuda:0")[offset:]
+    got = host(pg.pstream_add(tx, ty, z=z))
+    assert bits_equal(got, oracle.add_f32(x[offset:], y[offset:]))
+
+
+def test_stream_add_in_place():
+    say("stream add in place")
+    x, y = inputs.stream_inputs(1 << 20, 40, 41)
+    tx, ty = dev(x), dev(y)
+    pg.pstream_add(tx, ty, z=tx)
+    assert bits_equal(host(tx), oracle.add_f32(x, y))
+    tx2 = dev(x)
+    pg.pstream_add(tx2, ty, z=ty)
+    assert bits_equal(host(ty), oracle.add_f32(x, y))
+
+
+def test_stream_add_poisoned_output_overwritten():
+    say("stream add NaN-poisoned output")
+    x, y = inputs.stream_inputs(1 << 20, 42, 43)
+    z = torch.full((1 << 20,), float("nan"), device="cuda:0")
+    assert bits_equal(host(pg.pstream_add(dev(x), dev(y), z=z)), oracle.add_f32(x, y))
+
+
+def test_stream_add_scalar_full_size_in_place():
+    say("x + 1 8192x8192, out of place and in place")
+    x, _ = inputs.stream_inputs((8192, 8192))
+    ref = oracle.add_scalar_f32(x, 1.0)
+    tx = dev(x)
+    assert bits_equal(host(pg.pstream_add_scalar(tx, 1.0)), ref)
+    pg.pstream_add_scalar(tx, 1.0, z=tx)
+    assert bits_equal(host(tx), ref)
+
+
+@pytest.mark.parametrize("n", [1, 5, 1029, 262147])
+def test_stream_add_scalar_ragged_and_specials(n):
+    say("x + c n=%d" % n)
+    x = np.resize(np.concatenate([SPECIAL, inputs.uniform_f32(n, 50)]), n).astype(np.float32)
+    for c in (1.0, -0.0, 3.0e38):
+        assert bits_equal(host(pg.pstream_add_scalar(dev(x), c)), oracle.add_scalar_f32(x, c))
+
+
+# ------------------------------------------------------------ GEMM, element by element
+
+SMALL_SHAPES = [
+    (256, 256, 256),   # the 256^3 config: 128x128x64 tiles -> 2x2 grid, 4 K steps
+    (8, 8, 8),
+    (1, 8, 8),
+    (33, 40, 72),
+    (128, 128, 64),
+    (129, 136, 64),
+    (300, 264, 520),
+    (255, 248, 1000),
+    (520, 776, 136),
+    (64, 1024, 8),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL_SHAPES)
+def test_gemm_small_shapes_vs_full_oracle(M, N, K):
+    A, B = inputs.gemm_inputs(M, N, K)
+    ref, _ = oracle.gemm_f16(A, B)
+    outs = []
+    for v in VARIANTS:
+        got = gemm(A, B, v)
+        assert_close(got, ref, "M=%d N=%d K=%d variant %d" % (M, N, K, v))
+        outs.append(got)
+    # the K order inside an element does not depend on the tile size
+    assert bits_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("v", VARIANTS)
+def test_gemm_k_zero_gives_zeros(v):
+    say("gemm K=0")
+    C = torch.full((40, 24), float("nan"), dtype=torch.float16, device="cuda:0")
+    A = torch.empty((40, 0), dtype=torch.float16, device="cuda:0")
+    B = torch.empty((0, 24), dtype=torch.float16, device="cuda:0")
+    got = host(pg.pgemm_f16_variant(A, B, v, C=C))
+    assert np.all(got.view(np.uint16) == 0)
+
+
+def _finite_f16_no_negzero(rng, shape):
+    h = rng.integers(0, 65536, size=shape, dtype=np.uint32).astype(np.uint16)
+    h = h[((h & 0x7C00) != 0x7C00)]
+    h = np.resize(h, shape)
+    h[h == 0x8000] = 0
+    return h.view(np.float16)
+
+
+@pytest.mark.parametrize("v", VARIANTS)
+@pytest.mark.parametrize("M,N", [(256, 256), (296, 136)])
+def test_gemm_identity_bit_exact_with_subnormals(v, M, N):
+    rng = np.random.default_rng(60)
+    B = _finite_f16_no_negzero(rng, (M, N))
+    I = np.eye(M, dtype=np.float16)
+    ref, _ = oracle.gemm_f16(I, B)
+    got = gemm(I, B, v)
+    assert bits_equal(ref, B)  # the oracle's own closed form
+    assert bits_equal(got, ref), "identity: first mismatches %s" % np.argwhere(got.view(np.uint16) != ref.view(np.uint16))[:8]
+
+
+@pytest.mark.parametrize("v", VARIANTS)
+def test_gemm_permutation_bit_exact(v):
+    rng = np.random.default_rng(61)
+    M, N = 264, 200
+    perm = rng.permutation(M)
+    P = np.zeros((M, M), np.float16)
+    P[np.arange(M), perm] = 1
+    B = inputs.uniform_f16((M, N), 62)
+    got = gemm(P, B, v)
+    ref, _ = oracle.gemm_f16(P, B)
+    assert bits_equal(got, ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (2048, 2048, 32768), (8192, 8192, 8192)])
+def test_gemm_ones_full_size_exact(M, N, K):
+    say("gemm ones %dx%dx%d" % (M, N, K))
+    A = torch.ones((M, K), dtype=torch.float16, device="cuda:0")
+    B = torch.ones((K, N), dtype=torch.float16, device="cuda:0")
+    C = pg.pgemm_f16(A, B)
+    torch.cuda.synchronize()
+    assert bool((C == K).all().item())
+    # the oracle's closed form at the same K (a few elements)
+    ref, _ = oracle.gemm_f16(np.ones((2, K), np.float16), np.ones((K, 3), np.float16))
+    assert np.all(ref.astype(np.float64) == K)
+
+
+@pytest.mark.parametrize("K", [4096, 32768])
+def test_gemm_rank1_powers_of_two_exact(K):
+    say("gemm rank-1 K=%d" % K)
+    rng = np.random.default_rng(K + 1)
+    M, N = 264, 520
+    u = rng.choice([-1.0, -0.5, 0.5, 1.0], M)
+    v = rng.choice([-1.0, -0.5, 0.5, 1.0], N)
+    A = np.repeat(u[:, None], K, axis=1).astype(np.float16)
+    B = np.repeat(v[None, :], K, axis=0).astype(np.float16)
+    got = gemm(A, B)
+    assert np.array_equal(got.astype(np.float64), K * np.outer(u, v))
+
+
+@pytest.mark.parametrize("v", VARIANTS)
+def test_gemm_poisoned_output_overwritten(v):
+    A, B = inputs.gemm_inputs(300, 264, 136, seed_a=70, seed_b=71)
+    C = torch.full((300, 264), float("nan"), dtype=torch.float16, device="cuda:0")
+    got = gemm(A, B, v, C=C)
+    ref, _ = oracle.gemm_f16(A, B)
+    assert_close(got, ref, "poisoned C")
+
+
+def test_gemm_repeat_and_stream_determinism():
+    A, B = inputs.gemm_inputs(1024, 1024, 1024, seed_a=80, seed_b=81)
+    tA, tB = dev(A), dev(B)
+    first = host(pg.pgemm_f16(tA, tB))
+    for _ in range(3):
+        assert bits_equal(host(pg.pgemm_f16(tA, tB)), first)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        C = pg.pgemm_f16(tA, tB)
+    s.synchronize()
+    assert bits_equal(C.cpu().numpy(), first)
+
+
+def test_gemm_row_subset_consistency():
+    # Rows of a 256-row product equal the same rows of a 4096-row product
+    # made with the same tile configuration.
+    A, B = inputs.gemm_inputs(4096, 1024, 512, seed_a=90, seed_b=91)
+    for v in VARIANTS:
+        full = gemm(A, B, v)
+        part = gemm(A[:256], B, v)
+        assert bits_equal(full[:256], part)
+
+
+def test_gemm_device_pointer_checks():
+    say("gemm argument checks with device pointers")
+    L = pg.lib()
+    buf = torch.zeros(1 << 16, dtype=torch.float16, device="cuda:0")
+    p = buf.data_ptr()
+    s = None
+    assert L.pgemm_f16(p + 2, p + 4096, p + 8192, 8, 8, 8, s) == pg.PGEMM_EUNSUPPORTED
+    assert L.pgemm_f16(p, p + 4096, p + 64, 8, 8, 8, s) == pg.PGEMM_EINVAL
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ GEMM at full size (sampled)
+
+FULL_CONFIGS = [
+    ("4096^3 uniform", 4096, 4096, 4096, "uniform"),
+    ("8192^3 normal(0,1/sqrt(K))", 8192, 8192, 8192, "normal"),
+    ("2048x2048x32768 uniform (long K)", 2048, 2048, 32768, "uniform"),
+]
+
+
+@pytest.mark.parametrize("name,M,N,K,dist", FULL_CONFIGS, ids=[c[0] for c in FULL_CONFIGS])
+def test_gemm_full_size_sampled(name, M, N, K, dist):
+    say("gemm full size %s" % name)
+    A, B = inputs.gemm_inputs(M, N, K, dist)
+    got = gemm(A, B)  # automatic variant: what the benchmark times
+    I, J = inputs.sample_points(M, N, 8192)
+    ref, S = oracle.gemm_f16_points(A, B, I, J)
+    assert_close(got[I, J], ref, name)
+    # diagnostics on the sample: error in fp16 ulps of the oracle value
+    d = np.abs(got[I, J].view(np.uint16).astype(np.int64) - ref.view(np.uint16).astype(np.int64))
+    say("  sample %d points: max |ulp diff| %d, frac exact %.4f" % (I.size, d.max(), np.mean(d == 0)))
