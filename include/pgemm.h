@@ -74,11 +74,16 @@ int pgemm_f16(const void* A, const void* B, void* C,
  * Same as pgemm_f16 with the tile configuration forced (tests and
  * benchmarks).  `variant`:
  *   0  automatic choice (what pgemm_f16 does)
- *   1  256x256 output tile per workgroup, 64-deep K steps, 4 waves
- *   2  128x128 output tile per workgroup, 64-deep K steps, 4 waves (the
- *      128x128x64 tiling of the quickstart's matmul)
+ *   1  256x256 output tile per workgroup, 4 waves; LDS ring of 4 stages of
+ *      K 32 filled by global->LDS copies issued 3 steps ahead
+ *   2  128x128 output tile, otherwise as 1
+ *   3  256x256 output tile, 4 waves; 2 LDS stages of K 64 plus a register
+ *      stage (global loads 2 steps ahead)
+ *   4  128x128 output tile, otherwise as 3 (the 128x128x64 tiling of the
+ *      quickstart's matmul)
  * Every variant gives bit-identical results for the same inputs (the K
- * order inside each output element does not depend on the tiling).
+ * order inside each output element depends neither on the tiling nor on
+ * the pipeline).
  * Unknown variants return PGEMM_EUNSUPPORTED.
  */
 int pgemm_f16_variant(const void* A, const void* B, void* C,

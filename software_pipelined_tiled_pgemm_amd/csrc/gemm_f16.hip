@@ -8,15 +8,20 @@
 //    "Hopper 上的矩阵乘法内核"): one workgroup per BM x BN output tile; tiles
 //    are independent and unordered.  The block id is remapped so that the
 //    tiles one XCD runs share rows of A and columns of B in that XCD's L2.
-//  * Sequential K pipeline (the emit_pipeline grid over K): each step consumes
-//    an A slice [BM, 64] and a B slice [64, BN] from LDS.
-//  * copy_start early / copy_wait late with multiple buffers (Pallas
-//    software-pipelining guide, section 4): the global loads for step k+2 are
-//    issued into registers while step k computes, are written into the free
-//    LDS buffer during step k+1, and one barrier per step publishes them.
-//    With two LDS buffers plus the register stage, three steps are in flight.
+//  * Sequential K pipeline (the emit_pipeline grid over K): each step
+//    consumes an A slice [BM, BK] and a B slice [BK, BN] from LDS.
+//  * copy_start early / copy_wait late with several buffers (Pallas
+//    software-pipelining guide, section 4; max_concurrent_steps of the
+//    quickstart's emit_pipeline).  Two pipelines are implemented:
+//      - LDS-DMA pipeline (variants 1, 2): a ring of 4 LDS stages of BK = 32.
+//        copy_start is a buffer_load ... lds (global memory straight into
+//        LDS, no registers), issued 3 steps ahead; copy_wait is an s_waitcnt
+//        on this wave's own copies followed by the workgroup barrier.
+//      - register-staged pipeline (variants 3, 4): 2 LDS stages of BK = 64
+//        plus one register stage; global loads for step k+2 are in flight
+//        while step k computes.
 //  * Buffer release (the quickstart's delay_release discussion): an LDS
-//    buffer is overwritten only after every wave has passed the barrier that
+//    stage is refilled only after every wave has passed the barrier that
 //    follows its last ds_read of it.  MFMA operands are VGPRs, so no matrix
 //    instruction can still be reading LDS at that point.
 //  * fp32 accumulator in registers (the quickstart's ACC): 32x32 MFMA blocks
@@ -26,23 +31,15 @@
 //    out): fp32 -> fp16, written to LDS, then 16-byte coalesced row stores.
 //
 // Matrix instruction: v_mfma_f32_32x32x16_f16 (32x32 output block, 16-deep
-// K, 8 fp16 per lane per operand).  The kernel computes the transposed block
-// C^T = B^T A^T per MFMA (B^T as the row operand), so that each lane ends up
-// holding four consecutive columns of one row of C -- 8 contiguous bytes for
-// the epilogue.
+// K, 8 fp16 per lane per operand; lanes 0-31 carry K 0..7, lanes 32-63 K
+// 8..15).  Each MFMA computes the transposed block C^T = B^T A^T (B^T as the
+// row operand), so that each lane ends up holding four consecutive columns of
+// one row of C -- 8 contiguous bytes for the epilogue.  Every variant feeds
+// the MFMAs the same K blocks in the same order, so all variants produce
+// bit-identical results.
 //
-// LDS layout: both operands are stored K-contiguous: A as [BM][64] and B
-// transposed as Bt[BN][64], 128 bytes per row, in 16-byte chunks.  Chunk c of
-// row r lives at chunk position c ^ (r & 7).  Eight lanes that read the same
-// logical chunk of eight consecutive rows (MFMA fragment reads), and eight
-// lanes that write eight different chunks of one row (A copies, transposed B
-// writes), both touch eight different chunk positions: 16-byte accesses do
-// not collide on banks.
-//
-// B arrives row-major (N contiguous).  Each thread loads a KR x 8 block of B
-// (KR rows of K, 8 columns), transposes it in registers and writes 8 rows of
-// Bt.  A is copied as is.  Edge tiles: buffer loads return zero outside the
-// matrix (rows >= M, K >= K, columns >= N), stores are masked.
+// Edge tiles: buffer loads return zero outside the matrix (rows >= M,
+// K >= K, columns >= N); stores are masked.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -56,139 +53,63 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(8)));
+#define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kBK = 64;                 // K depth of one pipeline step
-constexpr int kRowBytes = kBK * 2;      // bytes per LDS operand row
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset that reads as zero
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
-
-template <int BM_, int BN_>
-struct Tile {
-    static constexpr int BM = BM_, BN = BN_;
-    static constexpr int WM = 2, WN = 2;                 // waves along M and N
-    static constexpr int T = 64 * WM * WN;               // threads per workgroup
-    static constexpr int TM = BM / WM, TN = BN / WN;     // per-wave tile
-    static constexpr int FM = TM / 32, FN = TN / 32;     // 32x32 blocks per wave
-    static constexpr int A_LD = BM * (kBK / 8) / T;      // 16-byte A chunks per thread
-    static constexpr int KR = kBK * BN / (8 * T);        // B rows per thread (4 or 8)
-    static constexpr int A_BYTES = BM * kRowBytes;
-    static constexpr int STAGE = (BM + BN) * kRowBytes;
-    static constexpr int LDS = 2 * STAGE;
-    static constexpr int C_CHUNKS = BN / 8;              // 16-byte chunks per C row
-    static_assert(KR == 4 || KR == 8, "B staging handles 4 or 8 rows per thread");
-    static_assert(BM * BN * 2 <= LDS, "epilogue tile must fit in the stage buffers");
-    static_assert((BM * BN / 8) % T == 0, "epilogue chunks must divide evenly");
-};
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             kRsrcWord3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
 }
 
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
-template <class TL>
-struct Stager {
-    u32x4 a[TL::A_LD];
-    u32x4 b[TL::KR];
-
-    // Issue the global loads of K step `k0` (copy_start).  Thread t copies A
-    // chunks t, t+T, ... (8 consecutive threads cover one 128-byte row
-    // segment) and a KR x 8 block of B: KR rows starting at kb*KR, columns
-    // nb*8 .. nb*8+7, with kb = t % (64/KR) and nb = t / (64/KR).
-    // Out-of-matrix pieces get an offset with bit 31 set: past the end of
-    // the buffer, so the load returns zeros.
-    __device__ __forceinline__ void load(const _Float16* A, const _Float16* B, int M, int N, int K,
-                                         int m0, int n0, int k0, int tid) {
-        const int rows_valid = min(TL::BM, M - m0);
-        const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(A + (int64_t)m0 * K + k0, (uint32_t)((rows_valid * (int64_t)K - k0) * 2));
-        const int kc = tid & 7;
-        const uint32_t a_mask = (k0 + kc * 8 < K) ? 0u : kOOB;
-        const uint32_t a_off0 = (uint32_t)(((tid >> 3) * K + kc * 8) * 2) | a_mask;
-        const uint32_t a_step = (uint32_t)((TL::T / 8) * K * 2);
-#pragma unroll
-        for (int r = 0; r < TL::A_LD; ++r) a[r] = buf_load16(ra, a_off0 + r * a_step);
-
-        const int kv = min(kBK, K - k0);
-        const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(B + (int64_t)k0 * N + n0, (uint32_t)(((int64_t)kv * N - n0) * 2));
-        constexpr int KG = kBK / TL::KR;  // row groups
-        const int kb = tid % KG, nb = tid / KG;
-        const uint32_t b_mask = (n0 + nb * 8 < N) ? 0u : kOOB;
-        const uint32_t b_off0 = (uint32_t)((kb * TL::KR * N + nb * 8) * 2) | b_mask;
-#pragma unroll
-        for (int r = 0; r < TL::KR; ++r) b[r] = buf_load16(rb, b_off0 + (uint32_t)(r * N * 2));
-    }
-
-    // Write the staged registers into one LDS stage (the compiler's vmcnt
-    // wait before the first write is the copy_wait); B is transposed on the
-    // way: column j of the thread's block becomes KR consecutive K values of
-    // Bt row nb*8 + j.
-    __device__ __forceinline__ void store(char* stage, int tid) const {
-        const int kc = tid & 7;
-#pragma unroll
-        for (int r = 0; r < TL::A_LD; ++r) {
-            const int row = (tid >> 3) + (TL::T / 8) * r;
-            *reinterpret_cast<u32x4*>(stage + row * kRowBytes + swz(row, kc) * 16) = a[r];
-        }
-        char* bt = stage + TL::A_BYTES;
-        constexpr int KG = kBK / TL::KR;
-        const int kb = tid % KG, nb = tid / KG;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int n = nb * 8 + j;
-            const int sh = (j & 1) * 16;
-            uint32_t h[TL::KR];
-#pragma unroll
-            for (int r = 0; r < TL::KR; ++r) h[r] = (b[r][j >> 1] >> sh) & 0xFFFFu;
-            if constexpr (TL::KR == 8) {
-                u32x4 v;
-                v[0] = h[0] | (h[1] << 16);
-                v[1] = h[2] | (h[3] << 16);
-                v[2] = h[4] | (h[5] << 16);
-                v[3] = h[6] | (h[7] << 16);
-                *reinterpret_cast<u32x4*>(bt + n * kRowBytes + swz(n, kb) * 16) = v;
-            } else {
-                u32x2 v;
-                v[0] = h[0] | (h[1] << 16);
-                v[1] = h[2] | (h[3] << 16);
-                *reinterpret_cast<u32x2*>(bt + n * kRowBytes + swz(n, kb >> 1) * 16 +
-                                          (kb & 1) * 8) = v;
-            }
-        }
-    }
-};
-
-// MFMA operand fragments of sub-step s (16 K values): lane (lr, lk) takes
-// row lr of each 32-row block, K values 16s + 8lk .. +7 (one 16-byte chunk).
-template <class TL>
-__device__ __forceinline__ void read_frags(const char* stage, int s, int wm, int wn, int lane,
-                                           half8 (&fa)[TL::FM], half8 (&fb)[TL::FN]) {
-    const int lr = lane & 31;
-    const int col = swz(lr, s * 2 + (lane >> 5)) * 16;  // same for every 32-row block
-    const char* pa = stage + (wm * TL::TM + lr) * kRowBytes + col;
-#pragma unroll
-    for (int i = 0; i < TL::FM; ++i)
-        fa[i] = *reinterpret_cast<const half8*>(pa + i * 32 * kRowBytes);
-    const char* pb = stage + TL::A_BYTES + (wn * TL::TN + lr) * kRowBytes + col;
-#pragma unroll
-    for (int j = 0; j < TL::FN; ++j)
-        fb[j] = *reinterpret_cast<const half8*>(pb + j * 32 * kRowBytes);
+// Raw buffer descriptor as four dwords (base, stride 0, size in bytes, gfx9
+// format word), for use as an SGPR quad operand.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4 r;
+    r[0] = (uint32_t)a;
+    r[1] = (uint32_t)(a >> 32) & 0xFFFFu;
+    r[2] = bytes <= 0 ? 0u : (uint32_t)bytes;
+    r[3] = (uint32_t)kRsrcWord3;
+    return r;
 }
 
-template <class TL>
-__device__ __forceinline__ void mfma_block(floatx16 (&acc)[TL::FN][TL::FM],
-                                           const half8 (&fa)[TL::FM], const half8 (&fb)[TL::FN]) {
-#pragma unroll
-    for (int j = 0; j < TL::FN; ++j)
-#pragma unroll
-        for (int i = 0; i < TL::FM; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[j][i], 0, 0, 0);
+// One 16-byte-per-lane copy from global memory straight into LDS: lane l's
+// 16 bytes at buffer offset `off` land at LDS byte address lds + 16*l; an
+// offset past the buffer size writes zeros.  Written as inline assembly so
+// the compiler does not treat later LDS reads as possibly aliasing it and
+// wait for every copy in flight: the pipeline orders copies and reads itself,
+// with explicit vmcnt waits and workgroup barriers.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t off, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(off), "s"(rsrc), "s"(lds)
+        : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const LDS_AS char*)p;
+}
+
+// s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left at their "no wait" maxima),
+// gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ floatx16 mfma(half8 row_op, half8 col_op, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(row_op, col_op, c, 0, 0, 0);
 }
 
 // Block id -> output tile.  Workgroups are dealt to the 8 XCDs round-robin,
@@ -210,17 +131,373 @@ __device__ __forceinline__ void tile_of_block(int b, int nwg, int tiles_m, int t
     tn = r / gm;
 }
 
-template <class TL, int WAVES_PER_EU>
-__global__ __launch_bounds__(TL::T) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
-void gemm_f16_kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
-                     _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
-                     int group_m) {
+// Drain: fp32 -> fp16 (RNE) into an LDS copy of the BM x BN tile, then
+// 16-byte row stores.  Lane (lr, lk) of block (j, i) holds row wm*TM+i*32+lr
+// and columns wn*TN+j*32+8g+4lk+q for accumulator element 4g+q.  The 16-byte
+// chunk c of LDS row r sits at chunk position c ^ (r mod chunks-per-row), so
+// the 32 lanes writing one column chunk of 32 rows spread over the banks.
+template <int BM, int BN, int TM, int TN, int FM, int FN, int T>
+__device__ __forceinline__ void drain(char* smem, floatx16 (&acc)[FN][FM], _Float16* C, int M,
+                                      int N, int m0, int n0, int tid, int wm, int wn) {
+    constexpr int CH = BN / 8;  // 16-byte chunks per C row
+    const int lane = tid & 63;
+    const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * TM + i * 32 + lr;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int chunk = (wn * TN + j * 32) / 8 + g;
+                const int pchunk = chunk ^ (row & (CH - 1));
+                const _Float16 h0 = (_Float16)acc[j][i][4 * g + 0];
+                const _Float16 h1 = (_Float16)acc[j][i][4 * g + 1];
+                const _Float16 h2 = (_Float16)acc[j][i][4 * g + 2];
+                const _Float16 h3 = (_Float16)acc[j][i][4 * g + 3];
+                u32x2 v;
+                v[0] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                v[1] = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                *reinterpret_cast<u32x2*>(smem + row * (BN * 2) + pchunk * 16 + lk * 8) = v;
+            }
+        }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < BM * CH / T; ++r) {
+        const int id = tid + T * r;
+        const int row = id / CH, chunk = id % CH;
+        const int pchunk = chunk ^ (row & (CH - 1));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * (BN * 2) + pchunk * 16);
+        const int m = m0 + row, n = n0 + chunk * 8;
+        if (m < M && n < N) *reinterpret_cast<u32x4*>(C + (int64_t)m * N + n) = v;
+    }
+}
+
+// ===========================================================================
+// LDS-DMA pipeline: 4-stage LDS ring, BK = 32, copies straight into LDS.
+// ===========================================================================
+namespace dm {
+
+constexpr int BK = 32;
+constexpr int STAGES = 4;
+constexpr int A_ROW = BK * 2;  // bytes per A row in a stage
+
+// A stage: row-major [BM][32] fp16, 64-byte rows of four 16-byte chunks;
+// logical chunk c of row r is stored at chunk position c ^ aswz(r).  The
+// fragment read of one wave touches, per group of 8 (or 16) lanes, 8 (16)
+// consecutive rows at one logical chunk; aswz spreads them over distinct
+// bank groups whether the LDS serves 128 or 256 bytes per cycle.
+__device__ __forceinline__ int aswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// B stage: blocks of 4 K rows x 16 columns (128 bytes, row-major inside),
+// block (kq, nb) at ((kq * BN/16) + nb) * 128.  One ds_read_b64_tr_b16 of 16
+// lanes reads exactly one block: lane i reads the 8 bytes of row i/4,
+// columns 4(i%4)..+3, and the transposing read hands lane j column j with
+// its 4 consecutive K values -- the MFMA operand layout.
+template <int BM_, int BN_>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int WM = 2, WN = 2;
+    static constexpr int T = 64 * WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int A_BYTES = BM * A_ROW;
+    static constexpr int B_BYTES = BK * BN * 2;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = STAGES * STAGE;
+    static constexpr int NB16 = BN / 16;
+    static constexpr int A_CP = A_BYTES / 1024 / (WM * WN);  // 1 KiB copies per wave per step
+    static constexpr int B_CP = B_BYTES / 1024 / (WM * WN);
+    static constexpr int CP = A_CP + B_CP;
+    static_assert(BM * BN * 2 <= LDS, "epilogue tile must fit in the stage ring");
+    static_assert(A_CP >= 1 && B_CP >= 1, "each wave copies part of both operands");
+};
+
+template <class TL>
+struct Copier {
+    // Per-lane byte offsets of this wave's copies, relative to the tile
+    // origin at K = 0, plus the K (A) or column (B) coordinate that decides
+    // whether the piece lies inside the matrix.
+    uint32_t a_off[TL::A_CP];
+    int a_k[TL::A_CP];
+    uint32_t b_off[TL::B_CP];
+
+    __device__ __forceinline__ void init(int lane, int wave, int K, int N, int n0) {
+#pragma unroll
+        for (int t = 0; t < TL::A_CP; ++t) {
+            const int p = (wave * TL::A_CP + t) * 64 + lane;  // 16-byte chunk in the stage
+            const int row = p >> 2;
+            const int c = (p & 3) ^ aswz(row);
+            a_off[t] = (uint32_t)((row * K + c * 8) * 2);
+            a_k[t] = c * 8;
+        }
+#pragma unroll
+        for (int t = 0; t < TL::B_CP; ++t) {
+            const int p = (wave * TL::B_CP + t) * 64 + lane;
+            const int blk = p >> 3, kq = blk / TL::NB16, nb = blk % TL::NB16;
+            const int r = (p >> 1) & 3, h = p & 1;
+            const int n = nb * 16 + h * 8;
+            b_off[t] = (n0 + n < N) ? (uint32_t)(((kq * 4 + r) * N + n) * 2) : kOOB;
+        }
+    }
+
+    // copy_start of step k0 into the stage at LDS byte address `stage`.
+    __device__ __forceinline__ void issue(const _Float16* A, const _Float16* B, int M, int N,
+                                          int K, int m0, int n0, int k0, uint32_t stage,
+                                          int wave) const {
+        const int rows_valid = min(TL::BM, M - m0);
+        const u32x4 ra =
+            rsrc_words(A + (int64_t)m0 * K + k0, ((int64_t)rows_valid * K - k0) * 2);
+        const int kleft = K - k0;
+#pragma unroll
+        for (int t = 0; t < TL::A_CP; ++t) {
+            const uint32_t off = (a_k[t] < kleft) ? a_off[t] : kOOB;
+            dma16(ra, off, stage + (wave * TL::A_CP + t) * 1024);
+        }
+        const int kv = min(BK, kleft);
+        const u32x4 rb = rsrc_words(B + (int64_t)k0 * N + n0, ((int64_t)kv * N - n0) * 2);
+#pragma unroll
+        for (int t = 0; t < TL::B_CP; ++t)
+            dma16(rb, b_off[t], stage + TL::A_BYTES + (wave * TL::B_CP + t) * 1024);
+    }
+};
+
+// Operand fragments of sub-step s (K values 16s .. 16s+15 of the stage).
+template <class TL>
+__device__ __forceinline__ void read_frags(const char* stage, int s, int wm, int wn, int lane,
+                                           half8 (&fa)[TL::FM], half8 (&fb)[TL::FN]) {
+    const int lr = lane & 31, lk = lane >> 5;
+    const char* pa = stage + (wm * TL::TM + lr) * A_ROW + (((2 * s + lk) ^ aswz(lr)) * 16);
+#pragma unroll
+    for (int i = 0; i < TL::FM; ++i)
+        fa[i] = *reinterpret_cast<const half8*>(pa + i * 32 * A_ROW);
+    // lane l: columns (l>>4 & 1)*16 + 32j within the wave tile, K quads
+    // 4s + 2lk + {0,1}
+    const int nb = (wn * TL::TN) / 16 + ((lane >> 4) & 1);
+    const int kq = 4 * s + 2 * lk;
+    const char* pb = stage + TL::A_BYTES + (kq * TL::NB16 + nb) * 128 + (lane & 15) * 8;
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) {
+        const char* q = pb + 2 * j * 128;
+        const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS fp16x4_t*)q);
+        const fp16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS fp16x4_t*)(q + TL::NB16 * 128));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        fb[j] = __builtin_bit_cast(half8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+    }
+}
+
+template <class TL>
+__device__ __forceinline__ void mfma_block(floatx16 (&acc)[TL::FN][TL::FM],
+                                           const half8 (&fa)[TL::FM], const half8 (&fb)[TL::FN]) {
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j)
+#pragma unroll
+        for (int i = 0; i < TL::FM; ++i) acc[j][i] = mfma(fb[j], fa[i], acc[j][i]);
+}
+
+template <class TL, int WPE>
+__global__ __launch_bounds__(TL::T) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
+            _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
+            int group_m) {
+    __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * TL::BM, n0 = tn * TL::BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    floatx16 acc[TL::FN][TL::FM];
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j)
+#pragma unroll
+        for (int i = 0; i < TL::FM; ++i) acc[j][i] = floatx16{};
+
+    const int nk = (K + BK - 1) / BK;
+    if (nk > 0) {
+        Copier<TL> cp;
+        cp.init(lane, wave, K, N, n0);
+        // Prologue: copy_start for steps 0..3, one per ring stage.  Steps
+        // past the end of K read as zeros and are never used.
+        const uint32_t ring = lds_addr(smem);
+#pragma unroll
+        for (int s = 0; s < STAGES; ++s)
+            cp.issue(A, B, M, N, K, m0, n0, s * BK, ring + s * TL::STAGE, wave);
+        wait_vmcnt<(STAGES - 1) * TL::CP>();  // this wave's copies of step 0 landed
+        __syncthreads();                      // ... and every other wave's
+
+        half8 fa[2][TL::FM], fb[2][TL::FN];
+        read_frags<TL>(smem, 0, wm, wn, lane, fa[0], fb[0]);
+
+        for (int kt = 0; kt < nk; ++kt) {
+            char* cur = smem + (kt & (STAGES - 1)) * TL::STAGE;
+            char* nxt = smem + ((kt + 1) & (STAGES - 1)) * TL::STAGE;
+            // sub-step 0 of step kt; fetch the operands of sub-step 1
+            read_frags<TL>(cur, 1, wm, wn, lane, fa[1], fb[1]);
+            mfma_block<TL>(acc, fa[0], fb[0]);
+            // copy_wait for step kt+1: this wave's copies of it are older
+            // than the two later steps still in flight; the barrier extends
+            // that to all waves and releases stage `cur` (no wave reads it
+            // after this point).
+            wait_vmcnt<2 * TL::CP>();
+            __syncthreads();
+            cp.issue(A, B, M, N, K, m0, n0, (kt + STAGES) * BK,
+                     ring + (kt & (STAGES - 1)) * TL::STAGE, wave);  // copy_start kt+4
+            // sub-step 1 of step kt; fetch sub-step 0 of step kt+1
+            read_frags<TL>(nxt, 0, wm, wn, lane, fa[0], fb[0]);
+            mfma_block<TL>(acc, fa[1], fb[1]);
+        }
+        wait_vmcnt<0>();  // drain the copies of the steps past the end
+    }
+    __syncthreads();  // every wave is done with the stage ring
+    drain<TL::BM, TL::BN, TL::TM, TL::TN, TL::FM, TL::FN, TL::T>(smem, acc, C, M, N, m0, n0, tid,
+                                                                 wm, wn);
+}
+
+}  // namespace dm
+
+// ===========================================================================
+// Register-staged pipeline: 2 LDS stages of BK = 64 plus a register stage.
+// ===========================================================================
+namespace rs {
+
+constexpr int BK = 64;
+constexpr int ROW = BK * 2;  // bytes per LDS operand row
+
+// Both operands stored K-contiguous: A as [BM][64] and B transposed as
+// Bt[BN][64], 128-byte rows of 16-byte chunks; chunk c of row r sits at
+// chunk position c ^ (r & 7).  Eight lanes reading one logical chunk of
+// eight consecutive rows (fragment reads) and eight lanes writing eight
+// chunks of one row (copies, transposed B writes) hit eight chunk positions.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+template <int BM_, int BN_>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int WM = 2, WN = 2;
+    static constexpr int T = 64 * WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int A_LD = BM * (BK / 8) / T;  // 16-byte A chunks per thread
+    static constexpr int KR = BK * BN / (8 * T);    // B rows per thread (4 or 8)
+    static constexpr int A_BYTES = BM * ROW;
+    static constexpr int STAGE = (BM + BN) * ROW;
+    static constexpr int LDS = 2 * STAGE;
+    static_assert(KR == 4 || KR == 8, "B staging handles 4 or 8 rows per thread");
+    static_assert(BM * BN * 2 <= LDS, "epilogue tile must fit in the stage buffers");
+};
+
+template <class TL>
+struct Stager {
+    u32x4 a[TL::A_LD];
+    u32x4 b[TL::KR];
+
+    // copy_start of K step k0 into registers.  Thread t copies A chunks t,
+    // t+T, ... (8 consecutive threads cover one 128-byte row segment) and a
+    // KR x 8 block of B: KR rows from kb*KR, columns nb*8 .. nb*8+7, with
+    // kb = t % (64/KR), nb = t / (64/KR).  Pieces outside the matrix get an
+    // offset with bit 31 set, past the end of the buffer: they read as zero.
+    __device__ __forceinline__ void load(const _Float16* A, const _Float16* B, int M, int N, int K,
+                                         int m0, int n0, int k0, int tid) {
+        const int rows_valid = min(TL::BM, M - m0);
+        const __amdgpu_buffer_rsrc_t ra =
+            make_rsrc(A + (int64_t)m0 * K + k0, ((int64_t)rows_valid * K - k0) * 2);
+        const int kc = tid & 7;
+        const uint32_t a_mask = (k0 + kc * 8 < K) ? 0u : kOOB;
+        const uint32_t a_off0 = (uint32_t)(((tid >> 3) * K + kc * 8) * 2) | a_mask;
+        const uint32_t a_step = (uint32_t)((TL::T / 8) * K * 2);
+#pragma unroll
+        for (int r = 0; r < TL::A_LD; ++r) a[r] = buf_load16(ra, a_off0 + r * a_step);
+
+        const int kv = min(BK, K - k0);
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(B + (int64_t)k0 * N + n0, ((int64_t)kv * N - n0) * 2);
+        constexpr int KG = BK / TL::KR;
+        const int kb = tid % KG, nb = tid / KG;
+        const uint32_t b_mask = (n0 + nb * 8 < N) ? 0u : kOOB;
+        const uint32_t b_off0 = (uint32_t)((kb * TL::KR * N + nb * 8) * 2) | b_mask;
+#pragma unroll
+        for (int r = 0; r < TL::KR; ++r) b[r] = buf_load16(rb, b_off0 + (uint32_t)(r * N * 2));
+    }
+
+    // Write the staged registers into one LDS stage (the compiler's vmcnt
+    // wait before the first write is the copy_wait); B is transposed on the
+    // way: column j of the thread's block becomes KR consecutive K values of
+    // Bt row nb*8 + j.
+    __device__ __forceinline__ void store(char* stage, int tid) const {
+        const int kc = tid & 7;
+#pragma unroll
+        for (int r = 0; r < TL::A_LD; ++r) {
+            const int row = (tid >> 3) + (TL::T / 8) * r;
+            *reinterpret_cast<u32x4*>(stage + row * ROW + swz(row, kc) * 16) = a[r];
+        }
+        char* bt = stage + TL::A_BYTES;
+        constexpr int KG = BK / TL::KR;
+        const int kb = tid % KG, nb = tid / KG;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int n = nb * 8 + j;
+            const int sh = (j & 1) * 16;
+            uint32_t h[TL::KR];
+#pragma unroll
+            for (int r = 0; r < TL::KR; ++r) h[r] = (b[r][j >> 1] >> sh) & 0xFFFFu;
+            if constexpr (TL::KR == 8) {
+                u32x4 v;
+                v[0] = h[0] | (h[1] << 16);
+                v[1] = h[2] | (h[3] << 16);
+                v[2] = h[4] | (h[5] << 16);
+                v[3] = h[6] | (h[7] << 16);
+                *reinterpret_cast<u32x4*>(bt + n * ROW + swz(n, kb) * 16) = v;
+            } else {
+                u32x2 v;
+                v[0] = h[0] | (h[1] << 16);
+                v[1] = h[2] | (h[3] << 16);
+                *reinterpret_cast<u32x2*>(bt + n * ROW + swz(n, kb >> 1) * 16 + (kb & 1) * 8) = v;
+            }
+        }
+    }
+};
+
+// Operand fragments of sub-step s (16 K values): lane (lr, lk) takes row lr
+// of each 32-row block, K values 16s + 8lk .. +7 (one 16-byte chunk).
+template <class TL>
+__device__ __forceinline__ void read_frags(const char* stage, int s, int wm, int wn, int lane,
+                                           half8 (&fa)[TL::FM], half8 (&fb)[TL::FN]) {
+    const int lr = lane & 31;
+    const int col = swz(lr, s * 2 + (lane >> 5)) * 16;  // same for every 32-row block
+    const char* pa = stage + (wm * TL::TM + lr) * ROW + col;
+#pragma unroll
+    for (int i = 0; i < TL::FM; ++i) fa[i] = *reinterpret_cast<const half8*>(pa + i * 32 * ROW);
+    const char* pb = stage + TL::A_BYTES + (wn * TL::TN + lr) * ROW + col;
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) fb[j] = *reinterpret_cast<const half8*>(pb + j * 32 * ROW);
+}
+
+template <class TL>
+__device__ __forceinline__ void mfma_block(floatx16 (&acc)[TL::FN][TL::FM],
+                                           const half8 (&fa)[TL::FM], const half8 (&fb)[TL::FN]) {
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j)
+#pragma unroll
+        for (int i = 0; i < TL::FM; ++i) acc[j][i] = mfma(fb[j], fa[i], acc[j][i]);
+}
+
+template <class TL, int WPE>
+__global__ __launch_bounds__(TL::T) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
+            _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
+            int group_m) {
     __shared__ __attribute__((aligned(16))) char smem[TL::LDS];
 
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * TL::BM, n0 = tn * TL::BN;
-
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -231,13 +508,13 @@ void gemm_f16_kernel(const _Float16* __restrict__ A, const _Float16* __restrict_
 #pragma unroll
         for (int i = 0; i < TL::FM; ++i) acc[j][i] = floatx16{};
 
-    const int nk = (K + kBK - 1) / kBK;
+    const int nk = (K + BK - 1) / BK;
     if (nk > 0) {
         Stager<TL> st;
         // Prologue: step 0 into LDS stage 0, step 1 in flight in registers.
         st.load(A, B, M, N, K, m0, n0, 0, tid);
         st.store(smem, tid);
-        if (nk > 1) st.load(A, B, M, N, K, m0, n0, kBK, tid);
+        if (nk > 1) st.load(A, B, M, N, K, m0, n0, BK, tid);
         __syncthreads();
 
         half8 fa[2][TL::FM], fb[2][TL::FN];
@@ -247,13 +524,13 @@ void gemm_f16_kernel(const _Float16* __restrict__ A, const _Float16* __restrict_
             char* cur = smem + (kt & 1) * TL::STAGE;
             char* nxt = smem + ((kt & 1) ^ 1) * TL::STAGE;
 #pragma unroll
-            for (int s = 0; s < kBK / 16; ++s) {
+            for (int s = 0; s < BK / 16; ++s) {
                 if (s == 1 && kt + 1 < nk) {
                     // The free stage was last read before the previous barrier.
                     st.store(nxt, tid);
-                    if (kt + 2 < nk) st.load(A, B, M, N, K, m0, n0, (kt + 2) * kBK, tid);
+                    if (kt + 2 < nk) st.load(A, B, M, N, K, m0, n0, (kt + 2) * BK, tid);
                 }
-                if (s < kBK / 16 - 1) {
+                if (s < BK / 16 - 1) {
                     read_frags<TL>(cur, s + 1, wm, wn, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
                 } else {
                     __syncthreads();  // publishes `nxt`, releases `cur`
@@ -264,60 +541,24 @@ void gemm_f16_kernel(const _Float16* __restrict__ A, const _Float16* __restrict_
         }
     }
     __syncthreads();  // every wave is done with the stage buffers
-
-    // Drain: fp32 -> fp16 (RNE) into an LDS copy of the C tile, then 16-byte
-    // row stores.  Lane (lr, lk) of block (j, i) holds row wm*TM+i*32+lr and
-    // columns wn*TN+j*32+8g+4lk+q for accumulator element 4g+q.
-    {
-        const int lr = lane & 31, lk = lane >> 5;
-#pragma unroll
-        for (int j = 0; j < TL::FN; ++j)
-#pragma unroll
-            for (int i = 0; i < TL::FM; ++i) {
-                const int row = wm * TL::TM + i * 32 + lr;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int chunk = (wn * TL::TN + j * 32) / 8 + g;
-                    const int pchunk = chunk ^ (row & (TL::C_CHUNKS - 1));
-                    u32x2 v;
-                    const _Float16 h0 = (_Float16)acc[j][i][4 * g + 0];
-                    const _Float16 h1 = (_Float16)acc[j][i][4 * g + 1];
-                    const _Float16 h2 = (_Float16)acc[j][i][4 * g + 2];
-                    const _Float16 h3 = (_Float16)acc[j][i][4 * g + 3];
-                    v[0] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                    v[1] = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-                    *reinterpret_cast<u32x2*>(smem + row * (TL::BN * 2) + pchunk * 16 + lk * 8) = v;
-                }
-            }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < TL::BM * TL::C_CHUNKS / TL::T; ++r) {
-        const int id = tid + TL::T * r;
-        const int row = id / TL::C_CHUNKS, chunk = id % TL::C_CHUNKS;
-        const int pchunk = chunk ^ (row & (TL::C_CHUNKS - 1));
-        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * (TL::BN * 2) + pchunk * 16);
-        const int m = m0 + row, n = n0 + chunk * 8;
-        if (m < M && n < N)
-            *reinterpret_cast<u32x4*>(C + (int64_t)m * N + n) = v;
-    }
+    drain<TL::BM, TL::BN, TL::TM, TL::TN, TL::FM, TL::FN, TL::T>(smem, acc, C, M, N, m0, n0, tid,
+                                                                 wm, wn);
 }
 
-template <class TL, int WPE>
-hipError_t launch(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                  hipStream_t stream) {
+}  // namespace rs
+
+template <class TL, class KernelFn>
+hipError_t launch(KernelFn kern, const void* A, const void* B, void* C, int64_t M, int64_t N,
+                  int64_t K, hipStream_t stream) {
     const int tiles_m = (int)((M + TL::BM - 1) / TL::BM);
     const int tiles_n = (int)((N + TL::BN - 1) / TL::BN);
     const int nwg = tiles_m * tiles_n;
     // Bands of 4 tile rows: a run of consecutive logical tiles then covers
     // 4 rows x (run/4) columns of tiles.
     const int group_m = tiles_m < 4 ? tiles_m : 4;
-    hipLaunchKernelGGL((gemm_f16_kernel<TL, WPE>), dim3(nwg), dim3(TL::T), 0, stream,
-                       static_cast<const _Float16*>(A), static_cast<const _Float16*>(B),
-                       static_cast<_Float16*>(C), (int)M, (int)N, (int)K, tiles_m, tiles_n,
-                       group_m);
+    hipLaunchKernelGGL(kern, dim3(nwg), dim3(TL::T), 0, stream, static_cast<const _Float16*>(A),
+                       static_cast<const _Float16*>(B), static_cast<_Float16*>(C), (int)M, (int)N,
+                       (int)K, tiles_m, tiles_n, group_m);
     return hipGetLastError();
 }
 
@@ -335,10 +576,22 @@ hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int
                            int64_t K, int variant, hipStream_t stream) {
     if (variant == kGemmAuto) variant = gemm_choose_variant(M, N, K);
     switch (variant) {
-        case kGemm256x256:
-            return launch<Tile<256, 256>, 1>(A, B, C, M, N, K, stream);
-        case kGemm128x128:
-            return launch<Tile<128, 128>, 2>(A, B, C, M, N, K, stream);
+        case kGemm256x256: {
+            using TL = dm::Tile<256, 256>;
+            return launch<TL>(dm::kernel<TL, 1>, A, B, C, M, N, K, stream);
+        }
+        case kGemm128x128: {
+            using TL = dm::Tile<128, 128>;
+            return launch<TL>(dm::kernel<TL, 2>, A, B, C, M, N, K, stream);
+        }
+        case kGemmRs256x256: {
+            using TL = rs::Tile<256, 256>;
+            return launch<TL>(rs::kernel<TL, 1>, A, B, C, M, N, K, stream);
+        }
+        case kGemmRs128x128: {
+            using TL = rs::Tile<128, 128>;
+            return launch<TL>(rs::kernel<TL, 2>, A, B, C, M, N, K, stream);
+        }
         default:
             return hipErrorInvalidValue;
     }

@@ -10,9 +10,11 @@ namespace pgemm {
 // GEMM tile configurations (ids match pgemm_f16_variant).
 enum GemmVariant : int {
     kGemmAuto = 0,
-    kGemm256x256 = 1,
-    kGemm128x128 = 2,
-    kGemmNumVariants = 2,
+    kGemm256x256 = 1,    // LDS-DMA pipeline, 4 stages of K 32
+    kGemm128x128 = 2,    // LDS-DMA pipeline, 4 stages of K 32
+    kGemmRs256x256 = 3,  // register-staged pipeline, 2 LDS stages of K 64
+    kGemmRs128x128 = 4,  // register-staged pipeline, 2 LDS stages of K 64
+    kGemmNumVariants = 4,
 };
 
 // Picks a concrete variant for a problem shape.

@@ -68,7 +68,7 @@ def bits_equal(a, b):
     return np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-VARIANTS = [1, 2]
+VARIANTS = [1, 2, 3, 4]
 
 
 # ------------------------------------------------------------ worked examples
@@ -211,8 +211,11 @@ def test_gemm_small_shapes_vs_full_oracle(M, N, K):
         got = gemm(A, B, v)
         assert_close(got, ref, "M=%d N=%d K=%d variant %d" % (M, N, K, v))
         outs.append(got)
-    # the K order inside an element does not depend on the tile size
-    assert bits_equal(outs[0], outs[1])
+    # the K order inside an element depends neither on the tile size nor on
+    # the pipeline (LDS-DMA ring vs register staging): any difference would
+    # be a race on a reused buffer
+    for o in outs[1:]:
+        assert bits_equal(outs[0], o)
 
 
 @pytest.mark.parametrize("v", VARIANTS)
