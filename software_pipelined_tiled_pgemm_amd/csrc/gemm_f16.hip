@@ -243,6 +243,25 @@ struct Copier {
         }
     }
 
+    // Copy number c (A copies first, then B) of step k0 into the stage at
+    // LDS byte address `stage`.
+    __device__ __forceinline__ void issue_one(int c, const _Float16* A, const _Float16* B, int M,
+                                              int N, int K, int m0, int n0, int k0, uint32_t stage,
+                                              int wave) const {
+        if (c < TL::A_CP) {
+            const int rows_valid = min(TL::BM, M - m0);
+            const u32x4 ra =
+                rsrc_words(A + (int64_t)m0 * K + k0, ((int64_t)rows_valid * K - k0) * 2);
+            const uint32_t off = (a_k[c] < K - k0) ? a_off[c] : kOOB;
+            dma16(ra, off, stage + (wave * TL::A_CP + c) * 1024);
+        } else {
+            const int t = c - TL::A_CP;
+            const int kv = min(BK, K - k0);
+            const u32x4 rb = rsrc_words(B + (int64_t)k0 * N + n0, ((int64_t)kv * N - n0) * 2);
+            dma16(rb, b_off[t], stage + TL::A_BYTES + (wave * TL::B_CP + t) * 1024);
+        }
+    }
+
     // copy_start of step k0 into the stage at LDS byte address `stage`.
     __device__ __forceinline__ void issue(const _Float16* A, const _Float16* B, int M, int N,
                                           int K, int m0, int n0, int k0, uint32_t stage,
@@ -265,37 +284,74 @@ struct Copier {
 };
 
 // Operand fragments of sub-step s (K values 16s .. 16s+15 of the stage).
+// A: lane (lr, lk) reads row lr of 32-row block i, K values 16s+8lk .. +7.
 template <class TL>
-__device__ __forceinline__ void read_frags(const char* stage, int s, int wm, int wn, int lane,
-                                           half8 (&fa)[TL::FM], half8 (&fb)[TL::FN]) {
+__device__ __forceinline__ half8 read_a(const char* stage, int s, int i, int wm, int lane) {
     const int lr = lane & 31, lk = lane >> 5;
     const char* pa = stage + (wm * TL::TM + lr) * A_ROW + (((2 * s + lk) ^ aswz(lr)) * 16);
-#pragma unroll
-    for (int i = 0; i < TL::FM; ++i)
-        fa[i] = *reinterpret_cast<const half8*>(pa + i * 32 * A_ROW);
-    // lane l: columns (l>>4 & 1)*16 + 32j within the wave tile, K quads
-    // 4s + 2lk + {0,1}
-    const int nb = (wn * TL::TN) / 16 + ((lane >> 4) & 1);
-    const int kq = 4 * s + 2 * lk;
-    const char* pb = stage + TL::A_BYTES + (kq * TL::NB16 + nb) * 128 + (lane & 15) * 8;
-#pragma unroll
-    for (int j = 0; j < TL::FN; ++j) {
-        const char* q = pb + 2 * j * 128;
-        const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS fp16x4_t*)q);
-        const fp16x4_t hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS fp16x4_t*)(q + TL::NB16 * 128));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        fb[j] = __builtin_bit_cast(half8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-    }
+    return *reinterpret_cast<const half8*>(pa + i * 32 * A_ROW);
 }
 
+// B: lane l takes column (l>>4 & 1)*16 + (l & 15) of 32-column block j and
+// K quads 4s+2lk and 4s+2lk+1 (two transposing reads).
 template <class TL>
-__device__ __forceinline__ void mfma_block(floatx16 (&acc)[TL::FN][TL::FM],
-                                           const half8 (&fa)[TL::FM], const half8 (&fb)[TL::FN]) {
+__device__ __forceinline__ half8 read_b(const char* stage, int s, int j, int wn, int lane) {
+    const int lk = lane >> 5;
+    const int nb = (wn * TL::TN) / 16 + 2 * j + ((lane >> 4) & 1);
+    const int kq = 4 * s + 2 * lk;
+    const char* q = stage + TL::A_BYTES + (kq * TL::NB16 + nb) * 128 + (lane & 15) * 8;
+    const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS fp16x4_t*)q);
+    const fp16x4_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS fp16x4_t*)(q + TL::NB16 * 128));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(half8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+
+// The operand reads of one sub-step, in the order the next half-step's MFMAs
+// consume them (B block 0 and every A block first, then the other B blocks):
+// unit u < FM+FN of the read sequence.
+template <class TL>
+__device__ __forceinline__ void read_unit(int u, const char* stage, int s, int wm, int wn, int lane,
+                                          half8 (&fa)[TL::FM], half8 (&fb)[TL::FN]) {
+    if (u == 0)
+        fb[0] = read_b<TL>(stage, s, 0, wn, lane);
+    else if (u <= TL::FM)
+        fa[u - 1] = read_a<TL>(stage, s, u - 1, wm, lane);
+    else
+        fb[u - TL::FM] = read_b<TL>(stage, s, u - TL::FM, wn, lane);
+}
+
+// One half-step: the FN x FM MFMAs on (fa, fb), j-major, with the operand
+// reads of the next half-step (into na, nb) placed one per MFMA slot from the
+// first slot on, and this wave's global->LDS copies in the slots after them.
+// sched_barrier pins the order, so every read has most of a half-step
+// (about 16 x 32 cycles) to land before its first use and the copies issue
+// in the matrix unit's shadow.
+template <class TL, bool COPY>
+__device__ __forceinline__ void half_step(floatx16 (&acc)[TL::FN][TL::FM], const half8 (&fa)[TL::FM],
+                                          const half8 (&fb)[TL::FN], const char* rstage, int rs,
+                                          half8 (&na)[TL::FM], half8 (&nb)[TL::FN], int wm, int wn,
+                                          int lane, const Copier<TL>& cp, const _Float16* A,
+                                          const _Float16* B, int M, int N, int K, int m0, int n0,
+                                          int k0, uint32_t cstage, int wave) {
+    constexpr int NR = TL::FM + TL::FN;  // read units
+    constexpr int NS = TL::FM * TL::FN;  // MFMA slots
 #pragma unroll
-    for (int j = 0; j < TL::FN; ++j)
+    for (int q = 0; q < NS; ++q) {
+        const int j = q / TL::FM, i = q % TL::FM;
+        acc[j][i] = mfma(fb[j], fa[i], acc[j][i]);
+        if (q < NR) read_unit<TL>(q, rstage, rs, wm, wn, lane, na, nb);
+        if constexpr (COPY) {
+            if (q >= NR && q - NR < TL::CP) cp.issue_one(q - NR, A, B, M, N, K, m0, n0, k0, cstage, wave);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (COPY) {
 #pragma unroll
-        for (int i = 0; i < TL::FM; ++i) acc[j][i] = mfma(fb[j], fa[i], acc[j][i]);
+        for (int c = NS - NR; c < TL::CP; ++c) {
+            if (c >= 0) cp.issue_one(c, A, B, M, N, K, m0, n0, k0, cstage, wave);
+        }
+    }
 }
 
 template <class TL, int WPE>
@@ -333,25 +389,27 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
         __syncthreads();                      // ... and every other wave's
 
         half8 fa[2][TL::FM], fb[2][TL::FN];
-        read_frags<TL>(smem, 0, wm, wn, lane, fa[0], fb[0]);
+#pragma unroll
+        for (int u = 0; u < TL::FM + TL::FN; ++u)
+            read_unit<TL>(u, smem, 0, wm, wn, lane, fa[0], fb[0]);
 
         for (int kt = 0; kt < nk; ++kt) {
-            char* cur = smem + (kt & (STAGES - 1)) * TL::STAGE;
-            char* nxt = smem + ((kt + 1) & (STAGES - 1)) * TL::STAGE;
+            const char* cur = smem + (kt & (STAGES - 1)) * TL::STAGE;
+            const char* nxt = smem + ((kt + 1) & (STAGES - 1)) * TL::STAGE;
             // sub-step 0 of step kt; fetch the operands of sub-step 1
-            read_frags<TL>(cur, 1, wm, wn, lane, fa[1], fb[1]);
-            mfma_block<TL>(acc, fa[0], fb[0]);
+            half_step<TL, false>(acc, fa[0], fb[0], cur, 1, fa[1], fb[1], wm, wn, lane, cp, A, B,
+                                 M, N, K, m0, n0, 0, 0, wave);
             // copy_wait for step kt+1: this wave's copies of it are older
             // than the two later steps still in flight; the barrier extends
             // that to all waves and releases stage `cur` (no wave reads it
             // after this point).
             wait_vmcnt<2 * TL::CP>();
             __syncthreads();
-            cp.issue(A, B, M, N, K, m0, n0, (kt + STAGES) * BK,
-                     ring + (kt & (STAGES - 1)) * TL::STAGE, wave);  // copy_start kt+4
-            // sub-step 1 of step kt; fetch sub-step 0 of step kt+1
-            read_frags<TL>(nxt, 0, wm, wn, lane, fa[0], fb[0]);
-            mfma_block<TL>(acc, fa[1], fb[1]);
+            // sub-step 1 of step kt; fetch sub-step 0 of step kt+1; copy_start
+            // of step kt+4 into the released stage
+            half_step<TL, true>(acc, fa[1], fb[1], nxt, 0, fa[0], fb[0], wm, wn, lane, cp, A, B, M,
+                                N, K, m0, n0, (kt + STAGES) * BK,
+                                ring + (kt & (STAGES - 1)) * TL::STAGE, wave);
         }
         wait_vmcnt<0>();  // drain the copies of the steps past the end
     }
