@@ -15,8 +15,9 @@
 //    quickstart's emit_pipeline).  Two pipelines are implemented:
 //      - LDS-DMA pipeline (variants 1, 2): a ring of 4 LDS stages of BK = 32.
 //        copy_start is a buffer_load ... lds (global memory straight into
-//        LDS, no registers), issued 3 steps ahead; copy_wait is an s_waitcnt
-//        on this wave's own copies followed by the workgroup barrier.
+//        LDS, no registers), issued about 3 steps ahead and spread over the
+//        MFMA slots; copy_wait is an s_waitcnt on this wave's own copies
+//        followed by the workgroup barrier.
 //      - register-staged pipeline (variants 3, 4): 2 LDS stages of BK = 64
 //        plus one register stage; global loads for step k+2 are in flight
 //        while step k computes.
@@ -323,15 +324,15 @@ __device__ __forceinline__ void read_unit(int u, const char* stage, int s, int w
 
 // One half-step: the FN x FM MFMAs on (fa, fb), j-major, with the operand
 // reads of the next half-step (into na, nb) placed one per MFMA slot from the
-// first slot on, and this wave's global->LDS copies in the slots after them.
-// sched_barrier pins the order, so every read has most of a half-step
-// (about 16 x 32 cycles) to land before its first use and the copies issue
-// in the matrix unit's shadow.
-template <class TL, bool COPY>
+// first slot on, and copies c0 .. c0+NC-1 of one step (global->LDS) in the
+// slots after them.  sched_barrier pins the order, so every read has most of
+// a half-step (about 16 x 32 cycles) to land before its first use and the
+// copies issue in the matrix unit's shadow.
+template <class TL, int NC>
 __device__ __forceinline__ void half_step(floatx16 (&acc)[TL::FN][TL::FM], const half8 (&fa)[TL::FM],
                                           const half8 (&fb)[TL::FN], const char* rstage, int rs,
                                           half8 (&na)[TL::FM], half8 (&nb)[TL::FN], int wm, int wn,
-                                          int lane, const Copier<TL>& cp, const _Float16* A,
+                                          int lane, const Copier<TL>& cp, int c0, const _Float16* A,
                                           const _Float16* B, int M, int N, int K, int m0, int n0,
                                           int k0, uint32_t cstage, int wave) {
     constexpr int NR = TL::FM + TL::FN;  // read units
@@ -341,17 +342,12 @@ __device__ __forceinline__ void half_step(floatx16 (&acc)[TL::FN][TL::FM], const
         const int j = q / TL::FM, i = q % TL::FM;
         acc[j][i] = mfma(fb[j], fa[i], acc[j][i]);
         if (q < NR) read_unit<TL>(q, rstage, rs, wm, wn, lane, na, nb);
-        if constexpr (COPY) {
-            if (q >= NR && q - NR < TL::CP) cp.issue_one(q - NR, A, B, M, N, K, m0, n0, k0, cstage, wave);
-        }
+        if (q >= NR && q - NR < NC) cp.issue_one(c0 + q - NR, A, B, M, N, K, m0, n0, k0, cstage, wave);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (COPY) {
 #pragma unroll
-        for (int c = NS - NR; c < TL::CP; ++c) {
-            if (c >= 0) cp.issue_one(c, A, B, M, N, K, m0, n0, k0, cstage, wave);
-        }
-    }
+    for (int c = NS - NR; c < NC; ++c)
+        if (c >= 0) cp.issue_one(c0 + c, A, B, M, N, K, m0, n0, k0, cstage, wave);
 }
 
 template <class TL, int WPE>
@@ -379,37 +375,48 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     if (nk > 0) {
         Copier<TL> cp;
         cp.init(lane, wave, K, N, n0);
-        // Prologue: copy_start for steps 0..3, one per ring stage.  Steps
-        // past the end of K read as zeros and are never used.
         const uint32_t ring = lds_addr(smem);
+        // Prologue: copy_start for steps 0..2 and the first half of step 3.
+        // Steps past the end of K read as zeros and are never used.
 #pragma unroll
-        for (int s = 0; s < STAGES; ++s)
+        for (int s = 0; s < STAGES - 1; ++s)
             cp.issue(A, B, M, N, K, m0, n0, s * BK, ring + s * TL::STAGE, wave);
-        wait_vmcnt<(STAGES - 1) * TL::CP>();  // this wave's copies of step 0 landed
-        __syncthreads();                      // ... and every other wave's
-
+#pragma unroll
+        for (int c = 0; c < TL::CP / 2; ++c)
+            cp.issue_one(c, A, B, M, N, K, m0, n0, (STAGES - 1) * BK,
+                         ring + (STAGES - 1) * TL::STAGE, wave);
+        // this wave's copies of step 0 landed (2.5 steps issued after it) ...
+        wait_vmcnt<(STAGES - 2) * TL::CP + TL::CP / 2>();
+        __syncthreads();  // ... and every other wave's
         half8 fa[2][TL::FM], fb[2][TL::FN];
 #pragma unroll
         for (int u = 0; u < TL::FM + TL::FN; ++u)
             read_unit<TL>(u, smem, 0, wm, wn, lane, fa[0], fb[0]);
 
+        // Each step's CP copies are issued in two halves (copies 0..CP/2-1 and
+        // CP/2..CP-1) in two consecutive half-steps, so the copy traffic is
+        // spread evenly over the K loop.
+        constexpr int H = TL::CP / 2;
         for (int kt = 0; kt < nk; ++kt) {
             const char* cur = smem + (kt & (STAGES - 1)) * TL::STAGE;
             const char* nxt = smem + ((kt + 1) & (STAGES - 1)) * TL::STAGE;
-            // sub-step 0 of step kt; fetch the operands of sub-step 1
-            half_step<TL, false>(acc, fa[0], fb[0], cur, 1, fa[1], fb[1], wm, wn, lane, cp, A, B,
-                                 M, N, K, m0, n0, 0, 0, wave);
+            const uint32_t refill = ring + ((kt - 1) & (STAGES - 1)) * TL::STAGE;
+            // sub-step 0 of step kt; fetch the operands of sub-step 1; second
+            // half of the copies of step kt+3 (into the stage released at the
+            // previous barrier)
+            half_step<TL, TL::CP - H>(acc, fa[0], fb[0], cur, 1, fa[1], fb[1], wm, wn, lane, cp, H,
+                                      A, B, M, N, K, m0, n0, (kt + STAGES - 1) * BK, refill, wave);
             // copy_wait for step kt+1: this wave's copies of it are older
-            // than the two later steps still in flight; the barrier extends
-            // that to all waves and releases stage `cur` (no wave reads it
-            // after this point).
+            // than the 2*CP copies issued since; the barrier extends that to
+            // all waves and releases stage `cur` (no wave reads it after this
+            // point).
             wait_vmcnt<2 * TL::CP>();
             __syncthreads();
-            // sub-step 1 of step kt; fetch sub-step 0 of step kt+1; copy_start
-            // of step kt+4 into the released stage
-            half_step<TL, true>(acc, fa[1], fb[1], nxt, 0, fa[0], fb[0], wm, wn, lane, cp, A, B, M,
-                                N, K, m0, n0, (kt + STAGES) * BK,
-                                ring + (kt & (STAGES - 1)) * TL::STAGE, wave);
+            // sub-step 1 of step kt; fetch sub-step 0 of step kt+1; first half
+            // of the copies of step kt+4 into the released stage
+            half_step<TL, H>(acc, fa[1], fb[1], nxt, 0, fa[0], fb[0], wm, wn, lane, cp, 0, A, B, M,
+                             N, K, m0, n0, (kt + STAGES) * BK,
+                             ring + (kt & (STAGES - 1)) * TL::STAGE, wave);
         }
         wait_vmcnt<0>();  // drain the copies of the steps past the end
     }
