@@ -23,7 +23,11 @@ int gemm_choose_variant(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N,
                            int64_t K, int variant, hipStream_t stream);
 
-constexpr int64_t kStreamDefaultBlock = 512 * 512;  // elements per workgroup block
+// Elements per workgroup block of the streaming kernels (the block-size knob
+// of the pipelined elementwise add), chosen by measurement on MI355X: small
+// one-shot blocks keep many workgroups, and so many 16-byte loads, in flight.
+constexpr int64_t kStreamDefaultBlock = 4096;
+constexpr int64_t kStreamScalarBlock = 8192;
 
 hipError_t launch_stream_add(const float* x, const float* y, float* z, int64_t n,
                              int64_t block_elems, hipStream_t stream);

@@ -11,7 +11,10 @@
 //
 // Each lane issues all of its 16-byte loads for an unrolled group before any
 // add (copy_start early), adds once the data is back (copy_wait late) and
-// stores; the next group's loads of other wavefronts overlap those stores.
+// stores; the loads of other workgroups overlap those stores.  With the
+// default block (4096 elements for x + y, 8192 for x + c) every lane does
+// exactly one such group.  Loads and stores are non-temporal: the data is
+// touched once, so it should not displace anything in the caches.
 // Arithmetic is one IEEE binary32 add per element (v_add_f32, RNE, denormals
 // kept), so results are bit-identical to any IEEE implementation.
 
@@ -132,7 +135,7 @@ hipError_t launch_stream_add(const float* x, const float* y, float* z, int64_t n
 hipError_t launch_stream_add_scalar(const float* x, float c, float* z, int64_t n,
                                     hipStream_t stream) {
     if (aligned16(x) && aligned16(z)) {
-        const int64_t block = kStreamDefaultBlock;
+        const int64_t block = kStreamScalarBlock;
         const int64_t blocks = (n + block - 1) / block;
         hipLaunchKernelGGL(addc_vec_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, x, c,
                            z, n, block);
