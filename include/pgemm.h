@@ -81,6 +81,8 @@ int pgemm_f16(const void* A, const void* B, void* C,
  *      stage (global loads 2 steps ahead)
  *   4  128x128 output tile, otherwise as 3 (the 128x128x64 tiling of the
  *      quickstart's matmul)
+ *   5  256x256 output tile, 8 waves (two per SIMD, 128x64 each), otherwise
+ *      as 1
  * Every variant gives bit-identical results for the same inputs (the K
  * order inside each output element depends neither on the tiling nor on
  * the pipeline).

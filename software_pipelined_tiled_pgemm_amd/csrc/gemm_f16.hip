@@ -137,9 +137,13 @@ __device__ __forceinline__ void tile_of_block(int b, int nwg, int tiles_m, int t
 // and columns wn*TN+j*32+8g+4lk+q for accumulator element 4g+q.  The 16-byte
 // chunk c of LDS row r sits at chunk position c ^ (r mod chunks-per-row), so
 // the 32 lanes writing one column chunk of 32 rows spread over the banks.
+// Pairs of values are converted with one packed RNE conversion
+// (v_cvt_pk_f16_f32).  Tiles fully inside C store without per-store masks.
 template <int BM, int BN, int TM, int TN, int FM, int FN, int T>
 __device__ __forceinline__ void drain(char* smem, floatx16 (&acc)[FN][FM], _Float16* C, int M,
                                       int N, int m0, int n0, int tid, int wm, int wn) {
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    typedef float float2_t __attribute__((ext_vector_type(2)));
     constexpr int CH = BN / 8;  // 16-byte chunks per C row
     const int lane = tid & 63;
     const int lr = lane & 31, lk = lane >> 5;
@@ -148,31 +152,48 @@ __device__ __forceinline__ void drain(char* smem, floatx16 (&acc)[FN][FM], _Floa
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int row = wm * TM + i * 32 + lr;
+            char* rowp = smem + row * (BN * 2) + lk * 8;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int chunk = (wn * TN + j * 32) / 8 + g;
                 const int pchunk = chunk ^ (row & (CH - 1));
-                const _Float16 h0 = (_Float16)acc[j][i][4 * g + 0];
-                const _Float16 h1 = (_Float16)acc[j][i][4 * g + 1];
-                const _Float16 h2 = (_Float16)acc[j][i][4 * g + 2];
-                const _Float16 h3 = (_Float16)acc[j][i][4 * g + 3];
+                const half2_t h01 = __builtin_convertvector(
+                    (float2_t{acc[j][i][4 * g + 0], acc[j][i][4 * g + 1]}), half2_t);
+                const half2_t h23 = __builtin_convertvector(
+                    (float2_t{acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]}), half2_t);
                 u32x2 v;
-                v[0] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                v[1] = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-                *reinterpret_cast<u32x2*>(smem + row * (BN * 2) + pchunk * 16 + lk * 8) = v;
+                v[0] = __builtin_bit_cast(uint32_t, h01);
+                v[1] = __builtin_bit_cast(uint32_t, h23);
+                *reinterpret_cast<u32x2*>(rowp + pchunk * 16) = v;
             }
         }
     __syncthreads();
+    // Thread t stores chunk t % CH of rows t / CH + (T / CH) * r.
+    constexpr int RSTEP = T / CH;
+    const int chunk = tid % CH, row0 = tid / CH;
+    const char* src = smem + row0 * (BN * 2);
+    _Float16* dst = C + (int64_t)(m0 + row0) * N + n0 + chunk * 8;
+    const int64_t dstep = (int64_t)RSTEP * N;
+    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+    if (interior) {
 #pragma unroll
-    for (int r = 0; r < BM * CH / T; ++r) {
-        const int id = tid + T * r;
-        const int row = id / CH, chunk = id % CH;
-        const int pchunk = chunk ^ (row & (CH - 1));
-        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * (BN * 2) + pchunk * 16);
-        const int m = m0 + row, n = n0 + chunk * 8;
-        if (m < M && n < N) *reinterpret_cast<u32x4*>(C + (int64_t)m * N + n) = v;
+        for (int r = 0; r < BM / RSTEP; ++r) {
+            const int row = row0 + RSTEP * r;
+            const int pchunk = chunk ^ (row & (CH - 1));
+            const u32x4 v =
+                *reinterpret_cast<const u32x4*>(src + r * RSTEP * (BN * 2) + pchunk * 16);
+            *reinterpret_cast<u32x4*>(dst + r * dstep) = v;
+        }
+    } else {
+        const bool col_ok = n0 + chunk * 8 < N;
+#pragma unroll
+        for (int r = 0; r < BM / RSTEP; ++r) {
+            const int row = row0 + RSTEP * r;
+            const int pchunk = chunk ^ (row & (CH - 1));
+            const u32x4 v =
+                *reinterpret_cast<const u32x4*>(src + r * RSTEP * (BN * 2) + pchunk * 16);
+            if (col_ok && m0 + row < M) *reinterpret_cast<u32x4*>(dst + r * dstep) = v;
+        }
     }
 }
 
@@ -197,10 +218,10 @@ __device__ __forceinline__ int aswz(int row) { return ((row >> 1) ^ (row >> 3)) 
 // lanes reads exactly one block: lane i reads the 8 bytes of row i/4,
 // columns 4(i%4)..+3, and the transposing read hands lane j column j with
 // its 4 consecutive K values -- the MFMA operand layout.
-template <int BM_, int BN_>
+template <int BM_, int BN_, int WM_ = 2, int WN_ = 2>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_;
-    static constexpr int WM = 2, WN = 2;
+    static constexpr int WM = WM_, WN = WN_;  // waves along M and N
     static constexpr int T = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 32, FN = TN / 32;
@@ -351,7 +372,7 @@ __device__ __forceinline__ void half_step(floatx16 (&acc)[TL::FN][TL::FM], const
 }
 
 template <class TL, int WPE>
-__global__ __launch_bounds__(TL::T) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+__global__ __launch_bounds__(TL::T, 1) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
             _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
             int group_m) {
@@ -363,7 +384,7 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / TL::WN, wn = wave % TL::WN;
 
     floatx16 acc[TL::FN][TL::FM];
 #pragma unroll
@@ -647,6 +668,10 @@ hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int
         }
         case kGemm128x128: {
             using TL = dm::Tile<128, 128>;
+            return launch<TL>(dm::kernel<TL, 2>, A, B, C, M, N, K, stream);
+        }
+        case kGemm256x256w8: {
+            using TL = dm::Tile<256, 256, 2, 4>;
             return launch<TL>(dm::kernel<TL, 2>, A, B, C, M, N, K, stream);
         }
         case kGemmRs256x256: {

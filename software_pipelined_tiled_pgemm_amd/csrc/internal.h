@@ -14,7 +14,8 @@ enum GemmVariant : int {
     kGemm128x128 = 2,    // LDS-DMA pipeline, 4 stages of K 32
     kGemmRs256x256 = 3,  // register-staged pipeline, 2 LDS stages of K 64
     kGemmRs128x128 = 4,  // register-staged pipeline, 2 LDS stages of K 64
-    kGemmNumVariants = 4,
+    kGemm256x256w8 = 5,  // LDS-DMA pipeline, 8 waves (2 per SIMD), 128x64 per wave
+    kGemmNumVariants = 5,
 };
 
 // Picks a concrete variant for a problem shape.
