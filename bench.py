@@ -7,6 +7,8 @@ MI355X.
 A step is one GEMM launch at 4096^3 on inputs already resident in HBM.  The
 timed region is exactly K steps on one stream, bracketed by device
 synchronisation, and timed with HIP events recorded on that stream.  The
+default warm-up (300 launches) lets the clock settle: throughput rises over
+the first ~200 launches of a cold process and is flat afterwards.  The
 streaming kernels get their own timed regions of K launches each (rotating
 over three buffer sets, so no launch re-reads what the previous one left in
 the caches).  Prints one JSON line.
@@ -35,8 +37,8 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--quick", action="store_true", help="headline GEMM only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -242,7 +244,8 @@ def main():
         others = []
         for (M, N, K, dist) in [(8192, 8192, 8192, "normal"), (2048, 2048, 32768, "uniform"),
                                 (256, 256, 256, "uniform")]:
-            r = gemm_case(pg, inputs, M, N, K, dist, max(5, args.steps // 5), 3, stream)
+            r = gemm_case(pg, inputs, M, N, K, dist, max(5, args.steps // 10), max(3, args.warmup // 10),
+                          stream)
             print("gemm %dx%dx%d: %.1f us, %.1f TFLOP/s" % (M, N, K, r["us_per_launch"], r["tflops"]),
                   file=sys.stderr, flush=True)
             others.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})

@@ -20,6 +20,8 @@ the passage of the pages it follows:
   its section 4: one IEEE binary32 addition per element.
 * ``fill_f32`` / ``iota_f32`` -- "Your first kernel" (42.0 everywhere) and
   "Parallel work with a grid" (0.0 .. n-1) of the quickstart.
+* ``sum_axis0_f32`` -- the guide's section 7.2 reduction: the output block
+  starts at zero and x[0], x[1], ... are added to it in order, in f32.
 * ``f16_from_f64`` / ``f64_from_f16`` -- the binary16 rounding and decoding
   used by the GEMM oracle, exposed so tests can pin them.
 """
@@ -68,6 +70,7 @@ def _load():
     lib.oracle_add_f32.argtypes = [p, p, p, i64]
     lib.oracle_add_scalar_f32.argtypes = [p, ctypes.c_float, p, i64]
     lib.oracle_fill_f32.argtypes = [p, ctypes.c_float, i64]
+    lib.oracle_sum_axis0_f32.argtypes = [p, p, i64, i64]
     lib.oracle_iota_f32.argtypes = [p, i64]
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -175,6 +178,19 @@ def add_scalar_f32(x, c: float) -> np.ndarray:
     z = np.empty_like(x)
     _load().oracle_add_scalar_f32(_ptr(x), ctypes.c_float(c), _ptr(z), x.size)
     return z
+
+
+def sum_axis0_f32(x) -> np.ndarray:
+    """o = x[0] + x[1] + ... + x[R-1] (first axis), f32, added in that order
+    starting from +0.0.  x: float32 of shape (R, ...)."""
+    x = _f32(x)
+    if x.ndim < 1:
+        raise ValueError("need at least one axis")
+    R = x.shape[0]
+    n = int(np.prod(x.shape[1:], dtype=np.int64))
+    o = np.empty(x.shape[1:], np.float32)
+    _load().oracle_sum_axis0_f32(_ptr(x), _ptr(o), R, n)
+    return o
 
 
 def fill_f32(n: int, v: float = 42.0) -> np.ndarray:

@@ -23,6 +23,12 @@
  *    every element.  The oracle is one IEEE-754 binary32 addition per element.
  *  - fill and iota.  Quickstart "Your first kernel" writes 42.0 into 128 f32
  *    elements; "Parallel work with a grid" writes 0.0, 1.0, ..., 1023.0.
+ *  - Reduction along the last grid axis.  The guide, section 7.2
+ *    "reductions and accumulation", sums an (R, M, N) f32 array over its
+ *    first array axis by making that axis the last (sequential) grid axis:
+ *    the output block is zeroed at the first step and x[i] is added to it
+ *    at step i, in f32.  The oracle is that loop: start from +0.0f and add
+ *    x[0], x[1], ..., x[R-1] in this order, one binary32 addition each.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math, so
  * the x86-64 SSE2 arithmetic is IEEE binary32/binary64 with RNE and no
@@ -209,6 +215,19 @@ void oracle_add_scalar_f32(const float* x, float c, float* z, int64_t n)
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i)
         z[i] = x[i] + c;
+}
+
+/* o[j] = (((0 + x[0][j]) + x[1][j]) + ...) + x[R-1][j], binary32, ascending
+ * i.  x is [R][n] row-major. */
+void oracle_sum_axis0_f32(const float* x, float* o, int64_t R, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j) {
+        float s = 0.0f;
+        for (int64_t i = 0; i < R; ++i)
+            s = s + x[i * n + j];
+        o[j] = s;
+    }
 }
 
 void oracle_fill_f32(float* o, float v, int64_t n)

@@ -325,3 +325,71 @@ def test_fill_pages_worked_example():
 
 def test_iota_pages_worked_example():
     assert _bits_equal_f32(oracle.iota_f32(1024), _golden.values_f32("iota_1024.txt"))
+
+
+# ---------------------------------------------------------------- reduction (guide 7.2)
+
+def test_sum_axis0_pages_worked_example():
+    g = _golden.keyed("sum_ones_8x1024x1024.txt")
+    shape = tuple(int(s) for s in g["shape"])
+    x = np.full(shape, float(g["operand"][0]), np.float32)
+    o = oracle.sum_axis0_f32(x)
+    assert o.shape == shape[1:]
+    assert np.all(o == np.float32(g["expected"][0]))
+
+
+def test_sum_axis0_order_is_ascending_sequential():
+    # 1 + 2^-24 rounds to 1 (tie to even), so adding two 2^-24 after the 1
+    # leaves 1.0; adding them first gives 2^-23, and 1 + 2^-23 is exact.
+    e = 2.0 ** -24
+    x = np.array([[1.0], [e], [e]], np.float32)
+    assert oracle.sum_axis0_f32(x)[0] == np.float32(1.0)
+    y = np.array([[e], [e], [1.0]], np.float32)
+    assert oracle.sum_axis0_f32(y)[0] == np.float32(1.0 + 2.0 ** -23)
+
+
+def test_sum_axis0_exact_integer_sums_and_signed_zero():
+    rng = np.random.default_rng(70)
+    x = rng.integers(-1000, 1000, size=(37, 5, 7)).astype(np.float32)
+    assert np.array_equal(oracle.sum_axis0_f32(x), x.astype(np.int64).sum(axis=0).astype(np.float32))
+    z = oracle.sum_axis0_f32(np.array([[-0.0, 0.0]], np.float32))
+    assert z.view(np.uint32)[0] == 0 and z.view(np.uint32)[1] == 0  # +0 start: -0 + ... -> +0
+    empty = oracle.sum_axis0_f32(np.zeros((0, 3), np.float32))
+    assert np.array_equal(empty.view(np.uint32), np.zeros(3, np.uint32))
+
+
+def test_sum_axis0_error_bound_random():
+    rng = np.random.default_rng(71)
+    x = rng.uniform(-1, 1, size=(64, 1000)).astype(np.float32)
+    o = oracle.sum_axis0_f32(x).astype(np.float64)
+    exact = x.astype(np.float64).sum(axis=0)
+    bound = 64 * 2.0 ** -24 * np.abs(x.astype(np.float64)).sum(axis=0)
+    assert np.all(np.abs(o - exact) <= bound)
+
+
+def _sum_reversed(x):
+    s = np.zeros(x.shape[1:], np.float32)
+    for i in range(x.shape[0] - 1, -1, -1):
+        s = (s + x[i]).astype(np.float32)
+    return s
+
+
+def _sum_pairwise(x):
+    parts = [x[i] for i in range(x.shape[0])]
+    while len(parts) > 1:
+        nxt = [(parts[k] + parts[k + 1]).astype(np.float32) for k in range(0, len(parts) - 1, 2)]
+        if len(parts) % 2:
+            nxt.append(parts[-1])
+        parts = nxt
+    return parts[0]
+
+
+@pytest.mark.parametrize("mutant", [_sum_reversed, _sum_pairwise])
+def test_sum_axis0_order_pin_rejects_other_orders(mutant):
+    # Plausible wrong oracles: the reduction axis walked backwards, or a
+    # pairwise tree.  On 1 followed by four 2^-24 the ascending sum is 1.0
+    # and both of these differ.
+    e = 2.0 ** -24
+    x = np.array([[1.0], [e], [e], [e], [e]], np.float32)
+    assert oracle.sum_axis0_f32(x)[0] == np.float32(1.0)
+    assert mutant(x)[0] != np.float32(1.0)
