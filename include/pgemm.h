@@ -132,6 +132,21 @@ int pstream_add_scalar(const float* x, float c, float* z, int64_t n,
                        pgemm_stream_t stream);
 
 /*
+ * o[j] = x[0][j] + x[1][j] + ... + x[R-1][j] for j in [0, n): the reduction
+ * of the Pallas software-pipelining guide, section 7.2, which sums an
+ * (R, M, N) array over its first axis by making that axis the last,
+ * sequential grid axis and zeroing the resident output block at its first
+ * step.  x is [R][n] row-major f32 (n = M*N), o is [n] f32.  The adds are
+ * binary32, in ascending i, starting from +0.0f, so the result equals the
+ * plain sequential loop bit for bit.  R == 0 writes +0.0 everywhere;
+ * n == 0 enqueues nothing.  o must not overlap x (PGEMM_EINVAL); null
+ * pointers with non-zero sizes and negative sizes are PGEMM_EINVAL;
+ * n > 2^36 or R*n > 2^40 is PGEMM_EUNSUPPORTED.  16-byte aligned x and o
+ * with n % 4 == 0 take the vector path.
+ */
+int preduce_sum_f32(const float* x, float* o, int64_t R, int64_t n, pgemm_stream_t stream);
+
+/*
  * Worked examples of the quickstart, exported for tests:
  *  pgemm_test_fill_f32: o[i] = v for i in [0, n) ("Your first kernel":
  *    128 elements of 42.0).

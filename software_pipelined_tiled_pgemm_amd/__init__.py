@@ -14,7 +14,7 @@ from ._lib import (PGEMM_EHIP, PGEMM_EINVAL, PGEMM_EUNSUPPORTED, PGEMM_OK, Pgemm
 
 __all__ = [
     "pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants",
-    "pstream_add", "pstream_add_blocked", "pstream_add_scalar",
+    "pstream_add", "pstream_add_blocked", "pstream_add_scalar", "preduce_sum_f32",
     "pgemm_test_fill_f32", "pgemm_test_iota_f32",
     "lib", "status_string", "PgemmError",
     "PGEMM_OK", "PGEMM_EINVAL", "PGEMM_EUNSUPPORTED", "PGEMM_EHIP",
@@ -128,6 +128,27 @@ def pstream_add_scalar(x, c, z=None, stream=None):
                                       _stream_handle(x.device, stream))
     _call(rc, "pstream_add_scalar")
     return z
+
+
+def preduce_sum_f32(x, out=None, stream=None):
+    """Sum of a float32 tensor of shape (R, ...) over its first axis, added
+    in ascending order from +0.0 (the guide's section 7.2 reduction)."""
+    torch = _torch()
+    _check_dev(x, torch.float32, "x")
+    if x.dim() < 1:
+        raise ValueError("x needs at least one dimension")
+    R = x.shape[0]
+    if out is None:
+        out = torch.empty(tuple(x.shape[1:]), dtype=torch.float32, device=x.device)
+    else:
+        _check_dev(out, torch.float32, "out")
+        if tuple(out.shape) != tuple(x.shape[1:]) or out.device != x.device:
+            raise ValueError("out must have shape %s on %s" % (tuple(x.shape[1:]), x.device))
+    with torch.cuda.device(x.device):
+        rc = lib().preduce_sum_f32(x.data_ptr(), out.data_ptr(), R, out.numel(),
+                                   _stream_handle(x.device, stream))
+    _call(rc, "preduce_sum_f32")
+    return out
 
 
 def pgemm_test_fill_f32(n, v=42.0, device="cuda", out=None, stream=None):

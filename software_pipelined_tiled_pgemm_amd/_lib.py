@@ -37,6 +37,7 @@ def _declare(lib):
         "pstream_add": (i32, [p, p, p, i64, p]),
         "pstream_add_blocked": (i32, [p, p, p, i64, i64, p]),
         "pstream_add_scalar": (i32, [p, ctypes.c_float, p, i64, p]),
+        "preduce_sum_f32": (i32, [p, p, i64, i64, p]),
         "pgemm_test_fill_f32": (i32, [p, ctypes.c_float, i64, p]),
         "pgemm_test_iota_f32": (i32, [p, i64, p]),
         "pgemm_status_string": (ctypes.c_char_p, [i32]),

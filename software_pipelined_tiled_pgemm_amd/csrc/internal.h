@@ -35,6 +35,7 @@ hipError_t launch_stream_add(const float* x, const float* y, float* z, int64_t n
 hipError_t launch_stream_add_scalar(const float* x, float c, float* z, int64_t n,
                                     hipStream_t stream);
 hipError_t launch_fill(float* o, float v, int64_t n, hipStream_t stream);
+hipError_t launch_sum_axis0(const float* x, float* o, int64_t R, int64_t n, hipStream_t stream);
 hipError_t launch_iota(float* o, int64_t n, hipStream_t stream);
 
 }  // namespace pgemm

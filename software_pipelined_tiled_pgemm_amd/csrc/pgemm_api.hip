@@ -97,6 +97,16 @@ int pstream_add_scalar(const float* x, float c, float* z, int64_t n, pgemm_strea
     return hip_status(pgemm::launch_stream_add_scalar(x, c, z, n, static_cast<hipStream_t>(stream)));
 }
 
+int preduce_sum_f32(const float* x, float* o, int64_t R, int64_t n, pgemm_stream_t stream) {
+    if (R < 0 || n < 0) return PGEMM_EINVAL;
+    if (n == 0) return PGEMM_OK;
+    if (!o || (R > 0 && !x)) return PGEMM_EINVAL;
+    if (n > ((int64_t)1 << 36) || R > ((int64_t)1 << 40) / n) return PGEMM_EUNSUPPORTED;
+    if (R > 0 && overlap(o, n * 4, x, R * n * 4)) return PGEMM_EINVAL;
+    return hip_status(pgemm::launch_sum_axis0(R > 0 ? x : o, o, R, n,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int pgemm_test_fill_f32(float* o, float v, int64_t n, pgemm_stream_t stream) {
     if (n < 0) return PGEMM_EINVAL;
     if (n == 0) return PGEMM_OK;

@@ -24,7 +24,7 @@ def test_header_declares_the_boundary():
     names = _lib.declared_functions()
     for n in ["pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants", "pstream_add",
               "pstream_add_blocked", "pstream_add_scalar", "pgemm_test_fill_f32",
-              "pgemm_test_iota_f32", "pgemm_status_string", "pgemm_last_hip_error",
+              "pgemm_test_iota_f32", "preduce_sum_f32", "pgemm_status_string", "pgemm_last_hip_error",
               "pgemm_version"]:
         assert n in names, n
 
@@ -104,6 +104,16 @@ def test_scalar_and_test_kernels_argument_checks(L):
     assert L.pgemm_test_fill_f32(0, 1.0, 0, None) == OK
     assert L.pgemm_test_iota_f32(0, 4, None) == EINVAL
     assert L.pgemm_test_iota_f32(A, -1, None) == EINVAL
+
+
+def test_reduce_argument_checks(L):
+    assert L.preduce_sum_f32(A, C, -1, 8, None) == EINVAL
+    assert L.preduce_sum_f32(A, C, 8, -8, None) == EINVAL
+    assert L.preduce_sum_f32(0, C, 8, 8, None) == EINVAL
+    assert L.preduce_sum_f32(A, 0, 8, 8, None) == EINVAL
+    assert L.preduce_sum_f32(A, A + 64, 8, 8, None) == EINVAL      # o inside x
+    assert L.preduce_sum_f32(A, C, 8, 0, None) == OK                # nothing to do
+    assert L.preduce_sum_f32(A, C, 1 << 30, 1 << 20, None) == EUNSUP
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -350,3 +350,43 @@ def test_gemm_full_size_sampled(name, M, N, K, dist):
     # diagnostics on the sample: error in fp16 ulps of the oracle value
     d = np.abs(got[I, J].view(np.uint16).astype(np.int64) - ref.view(np.uint16).astype(np.int64))
     say("  sample %d points: max |ulp diff| %d, frac exact %.4f" % (I.size, d.max(), np.mean(d == 0)))
+
+
+# ------------------------------------------------------------ reduction (guide 7.2)
+
+def test_sum_axis0_pages_worked_example():
+    say("sum over axis 0 of ones (8, 1024, 1024)")
+    g = _golden.keyed("sum_ones_8x1024x1024.txt")
+    shape = tuple(int(s) for s in g["shape"])
+    x = torch.full(shape, float(g["operand"][0]), dtype=torch.float32, device="cuda:0")
+    o = torch.full(shape[1:], float("nan"), dtype=torch.float32, device="cuda:0")
+    got = host(pg.preduce_sum_f32(x, out=o))
+    assert np.all(got == np.float32(g["expected"][0]))
+
+
+@pytest.mark.parametrize("R,shape", [(8, (1024, 1024)), (1, (100,)), (3, (64, 33)), (9, (4096,)),
+                                     (17, (255, 4)), (1000, (64,)), (2, (1,)), (13, (7, 3))])
+def test_sum_axis0_bit_exact_vs_oracle(R, shape):
+    say("sum axis 0 R=%d shape=%s" % (R, shape))
+    x = inputs.uniform_f32((R,) + shape, 60 + R)
+    got = host(pg.preduce_sum_f32(dev(x)))
+    assert bits_equal(got, oracle.sum_axis0_f32(x))
+
+
+def test_sum_axis0_order_and_empty():
+    e = 2.0 ** -24
+    x = np.array([[1.0] * 8, [e] * 8, [e] * 8, [e] * 8, [e] * 8], np.float32)
+    got = host(pg.preduce_sum_f32(dev(x)))
+    assert np.all(got == np.float32(1.0))  # ascending order from +0: stays 1.0
+    o = torch.full((8,), float("nan"), dtype=torch.float32, device="cuda:0")
+    z = host(pg.preduce_sum_f32(torch.empty((0, 8), dtype=torch.float32, device="cuda:0"), out=o))
+    assert np.array_equal(z.view(np.uint32), np.zeros(8, np.uint32))
+
+
+def test_sum_axis0_misaligned_view_scalar_path():
+    say("sum axis 0 misaligned")
+    R, n = 5, 1001
+    flat = inputs.uniform_f32(R * n + 1, 77)
+    tx = dev(flat)[1:].view(R, n)
+    got = host(pg.preduce_sum_f32(tx))
+    assert bits_equal(got, oracle.sum_axis0_f32(flat[1:].reshape(R, n)))
