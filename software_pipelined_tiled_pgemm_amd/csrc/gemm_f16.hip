@@ -13,11 +13,11 @@
 //  * copy_start early / copy_wait late with several buffers (Pallas
 //    software-pipelining guide, section 4; max_concurrent_steps of the
 //    quickstart's emit_pipeline).  Two pipelines are implemented:
-//      - LDS-DMA pipeline (variants 1, 2): a ring of 4 LDS stages of BK = 32.
-//        copy_start is a buffer_load ... lds (global memory straight into
-//        LDS, no registers), issued about 3 steps ahead and spread over the
-//        MFMA slots; copy_wait is an s_waitcnt on this wave's own copies
-//        followed by the workgroup barrier.
+//      - LDS-DMA pipeline (variants 1, 2, 5): a ring of 5 LDS stages of
+//        BK = 32.  copy_start is a buffer_load ... lds (global memory
+//        straight into LDS, no registers), issued 2 to 4 steps ahead and
+//        spread over the MFMA slots; copy_wait is an s_waitcnt on this
+//        wave's own copies followed by the workgroup barrier.
 //      - register-staged pipeline (variants 3, 4): 2 LDS stages of BK = 64
 //        plus one register stage; global loads for step k+2 are in flight
 //        while step k computes.
@@ -198,13 +198,23 @@ __device__ __forceinline__ void drain(char* smem, floatx16 (&acc)[FN][FM], _Floa
 }
 
 // ===========================================================================
-// LDS-DMA pipeline: 4-stage LDS ring, BK = 32, copies straight into LDS.
+// LDS-DMA pipeline: 5-stage LDS ring, BK = 32, copies straight into LDS.
 // ===========================================================================
 namespace dm {
 
 constexpr int BK = 32;
-constexpr int STAGES = 4;
+constexpr int STAGES = 5;
 constexpr int A_ROW = BK * 2;  // bytes per A row in a stage
+
+// The copy engine fetches whole 128-byte lines, four lanes (64 bytes) at a
+// time.  A copy runs at full rate (about 58 bytes per clock per CU, measured)
+// only when every four consecutive lanes read one 64-byte segment and both
+// halves of each line are read within a few instructions; with 64-byte row
+// pieces or quads that straddle two rows it runs at about half that.  Both
+// layouts below are chosen for this:
+//  * A rows are 64 bytes per stage, so the A copies of steps 2j and 2j+1 are
+//    issued in pairs, back to back: the two halves of the same lines.
+//  * B rows are copied whole, lanes running along the row.
 
 // A stage: row-major [BM][32] fp16, 64-byte rows of four 16-byte chunks;
 // logical chunk c of row r is stored at chunk position c ^ aswz(r).  A
@@ -217,11 +227,18 @@ constexpr int A_ROW = BK * 2;  // bytes per A row in a stage
 // so the global reads stay coalesced.
 __device__ __forceinline__ int aswz(int row) { return (row >> 2) & 3; }
 
-// B stage: blocks of 4 K rows x 16 columns (128 bytes, row-major inside),
-// block (kq, nb) at ((kq * BN/16) + nb) * 128.  One ds_read_b64_tr_b16 of 16
-// lanes reads exactly one block: lane i reads the 8 bytes of row i/4,
-// columns 4(i%4)..+3, and the transposing read hands lane j column j with
-// its 4 consecutive K values -- the MFMA operand layout.
+// B stage: row-major [32][BN] fp16 (K rows of BN*2 bytes); the 64-byte group
+// g of row r is stored at group position g ^ (r & 3), i.e. 16-byte chunk c at
+// c ^ bswz(r).  One ds_read_b64_tr_b16 of 16 lanes reads 4 K rows x 16
+// columns: lane i reads the 8 bytes of row i/4, columns 4(i%4)..+3, and the
+// transposing read hands lane j column j with its 4 consecutive K values --
+// the MFMA operand layout.  A wave reads 64 contiguous logical bytes of each
+// of rows 4q..4q+3 (and of 4q+8..4q+11); the swizzle spreads those rows over
+// the four 64-byte bank groups, so the read is conflict-free.  The XOR moves
+// whole 64-byte groups, so each lane quad of a copy still reads one 64-byte
+// global segment.
+__device__ __forceinline__ int bswz(int row) { return (row & 3) << 2; }
+
 template <int BM_, int BN_, int WM_ = 2, int WN_ = 2>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_;
@@ -231,21 +248,25 @@ struct Tile {
     static constexpr int FM = TM / 32, FN = TN / 32;
     static constexpr int A_BYTES = BM * A_ROW;
     static constexpr int B_BYTES = BK * BN * 2;
+    static constexpr int B_ROW = BN * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int LDS = STAGES * STAGE;
-    static constexpr int NB16 = BN / 16;
     static constexpr int A_CP = A_BYTES / 1024 / (WM * WN);  // 1 KiB copies per wave per step
     static constexpr int B_CP = B_BYTES / 1024 / (WM * WN);
     static constexpr int CP = A_CP + B_CP;
+    static constexpr int H = CP / 2;  // copies per half-step
     static_assert(BM * BN * 2 <= LDS, "epilogue tile must fit in the stage ring");
-    static_assert(A_CP >= 1 && B_CP >= 1, "each wave copies part of both operands");
+    static_assert(A_CP == H && B_CP == H && A_CP % 2 == 0,
+                  "the copy schedule issues one operand per half-step, A in pairs");
+    static_assert(LDS <= 160 * 1024, "LDS of one CU");
+    static_assert(FM * FN >= 2 * H, "every copy gets its own MFMA slot");
 };
 
 template <class TL>
 struct Copier {
     // Per-lane byte offsets of this wave's copies, relative to the tile
-    // origin at K = 0, plus the K (A) or column (B) coordinate that decides
-    // whether the piece lies inside the matrix.
+    // origin at K = 0, plus the K coordinate (A) that decides whether the
+    // piece lies inside the matrix; B pieces past column N read as zeros.
     uint32_t a_off[TL::A_CP];
     int a_k[TL::A_CP];
     uint32_t b_off[TL::B_CP];
@@ -253,7 +274,7 @@ struct Copier {
     __device__ __forceinline__ void init(int lane, int wave, int K, int N, int n0) {
 #pragma unroll
         for (int t = 0; t < TL::A_CP; ++t) {
-            const int p = (wave * TL::A_CP + t) * 64 + lane;  // 16-byte chunk in the stage
+            const int p = (wave * TL::A_CP + t) * 64 + lane;  // 16-byte chunk in the A stage
             const int row = p >> 2;
             const int c = (p & 3) ^ aswz(row);
             a_off[t] = (uint32_t)((row * K + c * 8) * 2);
@@ -261,51 +282,27 @@ struct Copier {
         }
 #pragma unroll
         for (int t = 0; t < TL::B_CP; ++t) {
-            const int p = (wave * TL::B_CP + t) * 64 + lane;
-            const int blk = p >> 3, kq = blk / TL::NB16, nb = blk % TL::NB16;
-            const int r = (p >> 1) & 3, h = p & 1;
-            const int n = nb * 16 + h * 8;
-            b_off[t] = (n0 + n < N) ? (uint32_t)(((kq * 4 + r) * N + n) * 2) : kOOB;
+            const int p = (wave * TL::B_CP + t) * 64 + lane;  // 16-byte chunk in the B stage
+            const int row = p / (TL::B_ROW / 16);
+            const int c = (p % (TL::B_ROW / 16)) ^ bswz(row);
+            const int n = c * 8;
+            b_off[t] = (n0 + n < N) ? (uint32_t)((row * N + n) * 2) : kOOB;
         }
     }
-
-    // Copy number c (A copies first, then B) of step k0 into the stage at
-    // LDS byte address `stage`.
-    __device__ __forceinline__ void issue_one(int c, const _Float16* A, const _Float16* B, int M,
-                                              int N, int K, int m0, int n0, int k0, uint32_t stage,
-                                              int wave) const {
-        if (c < TL::A_CP) {
-            const int rows_valid = min(TL::BM, M - m0);
-            const u32x4 ra =
-                rsrc_words(A + (int64_t)m0 * K + k0, ((int64_t)rows_valid * K - k0) * 2);
-            const uint32_t off = (a_k[c] < K - k0) ? a_off[c] : kOOB;
-            dma16(ra, off, stage + (wave * TL::A_CP + c) * 1024);
-        } else {
-            const int t = c - TL::A_CP;
-            const int kv = min(BK, K - k0);
-            const u32x4 rb = rsrc_words(B + (int64_t)k0 * N + n0, ((int64_t)kv * N - n0) * 2);
-            dma16(rb, b_off[t], stage + TL::A_BYTES + (wave * TL::B_CP + t) * 1024);
-        }
-    }
-
-    // copy_start of step k0 into the stage at LDS byte address `stage`.
-    __device__ __forceinline__ void issue(const _Float16* A, const _Float16* B, int M, int N,
-                                          int K, int m0, int n0, int k0, uint32_t stage,
-                                          int wave) const {
+    // A copy t of step k0 into the stage at LDS byte address `stage`.
+    __device__ __forceinline__ void issue_a(int t, const _Float16* A, int M, int K, int m0, int k0,
+                                            uint32_t stage, int wave) const {
         const int rows_valid = min(TL::BM, M - m0);
-        const u32x4 ra =
-            rsrc_words(A + (int64_t)m0 * K + k0, ((int64_t)rows_valid * K - k0) * 2);
-        const int kleft = K - k0;
-#pragma unroll
-        for (int t = 0; t < TL::A_CP; ++t) {
-            const uint32_t off = (a_k[t] < kleft) ? a_off[t] : kOOB;
-            dma16(ra, off, stage + (wave * TL::A_CP + t) * 1024);
-        }
-        const int kv = min(BK, kleft);
+        const u32x4 ra = rsrc_words(A + (int64_t)m0 * K + k0, ((int64_t)rows_valid * K - k0) * 2);
+        const uint32_t off = (a_k[t] < K - k0) ? a_off[t] : kOOB;
+        dma16(ra, off, stage + (wave * TL::A_CP + t) * 1024);
+    }
+    // B copy t of step k0 into the stage at LDS byte address `stage`.
+    __device__ __forceinline__ void issue_b(int t, const _Float16* B, int N, int K, int n0, int k0,
+                                            uint32_t stage, int wave) const {
+        const int kv = min(BK, K - k0);
         const u32x4 rb = rsrc_words(B + (int64_t)k0 * N + n0, ((int64_t)kv * N - n0) * 2);
-#pragma unroll
-        for (int t = 0; t < TL::B_CP; ++t)
-            dma16(rb, b_off[t], stage + TL::A_BYTES + (wave * TL::B_CP + t) * 1024);
+        dma16(rb, b_off[t], stage + TL::A_BYTES + (wave * TL::B_CP + t) * 1024);
     }
 };
 
@@ -318,17 +315,18 @@ __device__ __forceinline__ half8 read_a(const char* stage, int s, int i, int wm,
     return *reinterpret_cast<const half8*>(pa + i * 32 * A_ROW);
 }
 
-// B: lane l takes column (l>>4 & 1)*16 + (l & 15) of 32-column block j and
-// K quads 4s+2lk and 4s+2lk+1 (two transposing reads).
+// B: lane l takes column 16*((l>>4)&1) + (l&15) of 32-column block j and K
+// values 16s+8lk .. +7 (two transposing reads of 4 K rows each).
 template <class TL>
 __device__ __forceinline__ half8 read_b(const char* stage, int s, int j, int wn, int lane) {
-    const int lk = lane >> 5;
-    const int nb = (wn * TL::TN) / 16 + 2 * j + ((lane >> 4) & 1);
-    const int kq = 4 * s + 2 * lk;
-    const char* q = stage + TL::A_BYTES + (kq * TL::NB16 + nb) * 128 + (lane & 15) * 8;
+    const int lk = lane >> 5, i = lane & 15;
+    const int nb = (wn * TL::TN) / 16 + 2 * j + ((lane >> 4) & 1);  // 16-column block
+    const int row = 16 * s + 8 * lk + (i >> 2);
+    const int c = (2 * nb + ((i >> 1) & 1)) ^ bswz(row);
+    const char* q = stage + TL::A_BYTES + row * TL::B_ROW + c * 16 + (i & 1) * 8;
     const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS fp16x4_t*)q);
     const fp16x4_t hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS fp16x4_t*)(q + TL::NB16 * 128));
+        __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS fp16x4_t*)(q + 4 * TL::B_ROW));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return __builtin_bit_cast(half8, u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
@@ -349,17 +347,16 @@ __device__ __forceinline__ void read_unit(int u, const char* stage, int s, int w
 
 // One half-step: the FN x FM MFMAs on (fa, fb), j-major, with the operand
 // reads of the next half-step (into na, nb) placed one per MFMA slot from the
-// first slot on, and copies c0 .. c0+NC-1 of one step (global->LDS) in the
-// slots after them.  sched_barrier pins the order, so every read has most of
-// a half-step (about 16 x 32 cycles) to land before its first use and the
-// copies issue in the matrix unit's shadow.
-template <class TL, int NC>
+// first slot on, and the half-step's H copies (copy(0) .. copy(H-1),
+// global->LDS) spread evenly over the slots (copy c after MFMA
+// (2c+1)*NS/(2H)).  sched_barrier pins the order, so every read has most of
+// a half-step to land before its first use and the copies issue in the
+// matrix unit's shadow.
+template <class TL, class CopyFn>
 __device__ __forceinline__ void half_step(floatx16 (&acc)[TL::FN][TL::FM], const half8 (&fa)[TL::FM],
                                           const half8 (&fb)[TL::FN], const char* rstage, int rs,
                                           half8 (&na)[TL::FM], half8 (&nb)[TL::FN], int wm, int wn,
-                                          int lane, const Copier<TL>& cp, int c0, const _Float16* A,
-                                          const _Float16* B, int M, int N, int K, int m0, int n0,
-                                          int k0, uint32_t cstage, int wave) {
+                                          int lane, CopyFn copy) {
     constexpr int NR = TL::FM + TL::FN;  // read units
     constexpr int NS = TL::FM * TL::FN;  // MFMA slots
 #pragma unroll
@@ -367,20 +364,34 @@ __device__ __forceinline__ void half_step(floatx16 (&acc)[TL::FN][TL::FM], const
         const int j = q / TL::FM, i = q % TL::FM;
         acc[j][i] = mfma(fb[j], fa[i], acc[j][i]);
         if (q < NR) read_unit<TL>(q, rstage, rs, wm, wn, lane, na, nb);
-        if (q >= NR && q - NR < NC) cp.issue_one(c0 + q - NR, A, B, M, N, K, m0, n0, k0, cstage, wave);
+#pragma unroll
+        for (int c = 0; c < TL::H; ++c)
+            if (q == (2 * c + 1) * NS / (2 * TL::H)) copy(c);
         __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int c = NS - NR; c < NC; ++c)
-        if (c >= 0) cp.issue_one(c0 + c, A, B, M, N, K, m0, n0, k0, cstage, wave);
 }
 
+__device__ __forceinline__ int wrap5(int s) { return s >= STAGES ? s - STAGES : s; }
+
+// Copy schedule.  Step s lives in ring slot s mod 5.  The K loop runs in
+// periods of two steps (kt even, kt+1); a period issues the copies of steps
+// kt+4 and kt+5, one operand per half-step, H copies each:
+//   step kt,   first half:  B of kt+4
+//   step kt,   second half: A pairs 0 .. A_CP/2-1 of (kt+4, kt+5)
+//   step kt+1, first half:  A pairs A_CP/2 .. A_CP-1 of (kt+4, kt+5)
+//   step kt+1, second half: B of kt+5
+// Slot of kt+4 (= slot of kt-1) is free after the barrier in the middle of
+// step kt-1, slot of kt+5 (= slot of kt) after the one in the middle of step
+// kt, so every copy lands in a released slot.  The wait in the middle of step
+// kt covers step kt+1: for kt even its last copy (B) is 5H copies old, for kt
+// odd its last copy (an A pair's first half) is 4H+1 old.
 template <class TL, int WPE>
 __global__ __launch_bounds__(TL::T, 1) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
             _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
             int group_m) {
     __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
+    constexpr int H = TL::H;
 
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -401,47 +412,63 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
         Copier<TL> cp;
         cp.init(lane, wave, K, N, n0);
         const uint32_t ring = lds_addr(smem);
-        // Prologue: copy_start for steps 0..2 and the first half of step 3.
-        // Steps past the end of K read as zeros and are never used.
+        // A pairs t0 .. t0+A_CP/2-1 of steps (s, s+1) into slots (sa, sb).
+        auto a_pairs = [&](int q, int t0, int s, int sa, int sb) __attribute__((always_inline)) {
+            const int t = t0 + (q >> 1), h = q & 1;
+            cp.issue_a(t, A, M, K, m0, (s + h) * BK, ring + (h ? sb : sa) * TL::STAGE, wave);
+        };
+        // Prologue: steps 0..3, in the order a period issues them.
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
-            cp.issue(A, B, M, N, K, m0, n0, s * BK, ring + s * TL::STAGE, wave);
+        for (int e = 0; e < 4; e += 2) {
 #pragma unroll
-        for (int c = 0; c < TL::CP / 2; ++c)
-            cp.issue_one(c, A, B, M, N, K, m0, n0, (STAGES - 1) * BK,
-                         ring + (STAGES - 1) * TL::STAGE, wave);
-        // this wave's copies of step 0 landed (2.5 steps issued after it) ...
-        wait_vmcnt<(STAGES - 2) * TL::CP + TL::CP / 2>();
-        __syncthreads();  // ... and every other wave's
+            for (int t = 0; t < H; ++t) cp.issue_b(t, B, N, K, n0, e * BK, ring + e * TL::STAGE, wave);
+#pragma unroll
+            for (int q = 0; q < 2 * H; ++q) a_pairs(q, 0, e, e, e + 1);
+#pragma unroll
+            for (int t = 0; t < H; ++t)
+                cp.issue_b(t, B, N, K, n0, (e + 1) * BK, ring + (e + 1) * TL::STAGE, wave);
+        }
+        wait_vmcnt<5 * H>();  // this wave's copies of step 0 landed ...
+        __syncthreads();      // ... and every other wave's
         half8 fa[2][TL::FM], fb[2][TL::FN];
 #pragma unroll
         for (int u = 0; u < TL::FM + TL::FN; ++u)
             read_unit<TL>(u, smem, 0, wm, wn, lane, fa[0], fb[0]);
 
-        // Each step's CP copies are issued in two halves (copies 0..CP/2-1 and
-        // CP/2..CP-1) in two consecutive half-steps, so the copy traffic is
-        // spread evenly over the K loop.
-        constexpr int H = TL::CP / 2;
-        for (int kt = 0; kt < nk; ++kt) {
-            const char* cur = smem + (kt & (STAGES - 1)) * TL::STAGE;
-            const char* nxt = smem + ((kt + 1) & (STAGES - 1)) * TL::STAGE;
-            const uint32_t refill = ring + ((kt - 1) & (STAGES - 1)) * TL::STAGE;
-            // sub-step 0 of step kt; fetch the operands of sub-step 1; second
-            // half of the copies of step kt+3 (into the stage released at the
-            // previous barrier)
-            half_step<TL, TL::CP - H>(acc, fa[0], fb[0], cur, 1, fa[1], fb[1], wm, wn, lane, cp, H,
-                                      A, B, M, N, K, m0, n0, (kt + STAGES - 1) * BK, refill, wave);
-            // copy_wait for step kt+1: this wave's copies of it are older
-            // than the 2*CP copies issued since; the barrier extends that to
-            // all waves and releases stage `cur` (no wave reads it after this
-            // point).
-            wait_vmcnt<2 * TL::CP>();
+        // Whole periods only: with an odd number of steps the last period's
+        // second step multiplies the zeros its copies read past the end of
+        // K, which leaves every accumulator unchanged (they start at +0 and
+        // never become -0, so adding +0 is exact).
+        int se = 0;  // slot of step kt
+        for (int kt = 0; kt < nk; kt += 2) {
+            const int s1 = wrap5(se + 1), s2 = wrap5(se + 2), s4 = wrap5(se + 4);
+            const char* cur = smem + se * TL::STAGE;
+            const char* nxt = smem + s1 * TL::STAGE;
+            // step kt, sub-step 0; read sub-step 1; B of step kt+4
+            half_step<TL>(acc, fa[0], fb[0], cur, 1, fa[1], fb[1], wm, wn, lane,
+                          [&](int q) __attribute__((always_inline)) {
+                              cp.issue_b(q, B, N, K, n0, (kt + 4) * BK, ring + s4 * TL::STAGE, wave);
+                          });
+            // copy_wait for step kt+1; the barrier also releases slot se
+            wait_vmcnt<5 * H>();
             __syncthreads();
-            // sub-step 1 of step kt; fetch sub-step 0 of step kt+1; first half
-            // of the copies of step kt+4 into the released stage
-            half_step<TL, H>(acc, fa[1], fb[1], nxt, 0, fa[0], fb[0], wm, wn, lane, cp, 0, A, B, M,
-                             N, K, m0, n0, (kt + STAGES) * BK,
-                             ring + (kt & (STAGES - 1)) * TL::STAGE, wave);
+            // step kt, sub-step 1; read sub-step 0 of step kt+1; first A pairs
+            half_step<TL>(acc, fa[1], fb[1], nxt, 0, fa[0], fb[0], wm, wn, lane,
+                          [&](int q) __attribute__((always_inline)) { a_pairs(q, 0, kt + 4, s4, se); });
+            // step kt+1, sub-step 0; read sub-step 1; other A pairs
+            half_step<TL>(acc, fa[0], fb[0], nxt, 1, fa[1], fb[1], wm, wn, lane,
+                          [&](int q) __attribute__((always_inline)) {
+                              a_pairs(q, TL::A_CP / 2, kt + 4, s4, se);
+                          });
+            // copy_wait for step kt+2; the barrier also releases slot s1
+            wait_vmcnt<4 * H>();
+            __syncthreads();
+            // step kt+1, sub-step 1; read sub-step 0 of step kt+2; B of step kt+5
+            half_step<TL>(acc, fa[1], fb[1], smem + s2 * TL::STAGE, 0, fa[0], fb[0], wm, wn, lane,
+                          [&](int q) __attribute__((always_inline)) {
+                              cp.issue_b(q, B, N, K, n0, (kt + 5) * BK, ring + se * TL::STAGE, wave);
+                          });
+            se = s2;
         }
         wait_vmcnt<0>();  // drain the copies of the steps past the end
     }
