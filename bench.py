@@ -52,7 +52,8 @@ def parse():
 def profile_run(pg, inputs):
     """Launch sequence for counter collection: one plain copy of known size
     (512 MiB read + 512 MiB written) to calibrate FETCH_SIZE / WRITE_SIZE,
-    then 3 launches each of the 4096^3 GEMM, the streaming add and x + 1."""
+    then 3 launches each of the 4096^3 GEMM, the streaming add, x + 1 and the
+    (8, 4096, 4096) reduction."""
     import torch
     src = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -71,6 +72,11 @@ def profile_run(pg, inputs):
         pg.pstream_add(tx, ty, z=tz)
     for _ in range(3):
         pg.pstream_add_scalar(tx, 1.0, z=tz)
+    del tx, ty, tz
+    xr = torch.from_numpy(inputs.uniform_f32((8, 4096, 4096), 0)).cuda()
+    o = torch.empty((4096, 4096), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        pg.preduce_sum_f32(xr, out=o)
     torch.cuda.synchronize()
     print("profile launches done", flush=True)
 
@@ -144,6 +150,23 @@ def stream_case(pg, inputs, steps, warmup, stream, scalar):
     gbs = bytes_per * steps / secs / 1e9
     return {"n": n, "bytes_per_launch": bytes_per, "us_per_launch": secs / steps * 1e6,
             "GB/s": gbs, "frac_of_hbm": gbs / PEAK_HBM_GBS}
+
+
+def reduce_case(pg, inputs, steps, warmup, stream):
+    """The guide's section 7.2 reduction at (8, 4096, 4096) f32: 8 slices of
+    64 MiB summed over the first axis; 9 * 64 MiB move per launch."""
+    import torch
+    R, M, N = 8, 4096, 4096
+    sets = [torch.from_numpy(inputs.uniform_f32((R, M, N), s)).cuda() for s in (0, 1)]
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    secs = time_launches(lambda i: pg.preduce_sum_f32(sets[i % 2], out=out), steps, warmup, stream)
+    bytes_per = 4.0 * (R + 1) * M * N
+    gbs = bytes_per * steps / secs / 1e9
+    return {"workload": "sum over axis 0 of (8, 4096, 4096) f32, U[-1,1], 2 rotating inputs",
+            "value": round(gbs, 1), "unit": "GB/s", "us_per_launch": round(secs / steps * 1e6, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("sum_axis0_vec_kernel", kernel_source_hash())}}
 
 
 def cpu_baseline(inputs, target_seconds):
@@ -241,6 +264,9 @@ def main():
                          "us_per_launch": round(addc["us_per_launch"], 2),
                          "frac": round(addc["frac_of_hbm"], 4)},
         }
+        out["reduction"] = reduce_case(pg, inputs, max(5, args.steps // 5), max(3, args.warmup // 5),
+                                       stream)
+        print("reduction: %.1f GB/s" % out["reduction"]["value"], file=sys.stderr, flush=True)
         others = []
         for (M, N, K, dist) in [(8192, 8192, 8192, "normal"), (2048, 2048, 32768, "uniform"),
                                 (256, 256, 256, "uniform")]:

@@ -74,8 +74,8 @@ int pgemm_f16(const void* A, const void* B, void* C,
  * Same as pgemm_f16 with the tile configuration forced (tests and
  * benchmarks).  `variant`:
  *   0  automatic choice (what pgemm_f16 does)
- *   1  256x256 output tile per workgroup, 4 waves; LDS ring of 4 stages of
- *      K 32 filled by global->LDS copies issued 3 steps ahead
+ *   1  256x256 output tile per workgroup, 4 waves; LDS ring of 5 stages of
+ *      K 32 filled by global->LDS copies issued 2 to 4 steps ahead
  *   2  128x128 output tile, otherwise as 1
  *   3  256x256 output tile, 4 waves; 2 LDS stages of K 64 plus a register
  *      stage (global loads 2 steps ahead)
@@ -94,6 +94,21 @@ int pgemm_f16_variant(const void* A, const void* B, void* C,
 
 /* Number of GEMM variants accepted by pgemm_f16_variant (largest id). */
 int pgemm_f16_num_variants(void);
+
+/*
+ * The variant (1 .. pgemm_f16_num_variants()) that pgemm_f16 uses for an
+ * M x N x K problem: the fastest variant on the nearest shape of the tuned
+ * table built into the library.  The table is written by the autotuner
+ * (software_pipelined_tiled_pgemm_amd/autotune.py), which times every
+ * variant -- tile shape, pipeline depth and wave count -- on a set of
+ * shapes; the pages name block size as the main tuning knob (software
+ * pipelining guide, section 6.1) and advise autotuning the number of
+ * concurrent copies (Chinese quickstart, section on emit_pipeline's key
+ * parameters).  Nearest means the smallest sum of |log2| ratios over M, N
+ * and K.  Pure host function: no HIP call, no device needed.
+ * Returns PGEMM_EINVAL for a negative size.
+ */
+int pgemm_f16_choose_variant(int64_t M, int64_t N, int64_t K);
 
 /*
  * z[i] = x[i] + y[i], i in [0, n): one IEEE binary32 addition per element,

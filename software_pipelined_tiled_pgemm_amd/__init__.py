@@ -13,7 +13,7 @@ from ._lib import (PGEMM_EHIP, PGEMM_EINVAL, PGEMM_EUNSUPPORTED, PGEMM_OK, Pgemm
                    lib, status_string)
 
 __all__ = [
-    "pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants",
+    "pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants", "pgemm_f16_choose_variant",
     "pstream_add", "pstream_add_blocked", "pstream_add_scalar", "preduce_sum_f32",
     "pgemm_test_fill_f32", "pgemm_test_iota_f32",
     "lib", "status_string", "PgemmError",
@@ -82,6 +82,14 @@ def pgemm_f16_variant(A, B, variant, C=None, stream=None):
 
 def pgemm_f16_num_variants():
     return lib().pgemm_f16_num_variants()
+
+
+def pgemm_f16_choose_variant(M, N, K):
+    """The variant pgemm_f16 runs for an M x N x K problem (host only)."""
+    rc = lib().pgemm_f16_choose_variant(int(M), int(N), int(K))
+    if rc < 0:
+        raise PgemmError(rc, "pgemm_f16_choose_variant")
+    return rc
 
 
 def _elementwise_out(x, z):

@@ -43,6 +43,7 @@
 // K >= K, columns >= N); stores are masked.
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "internal.h"
@@ -681,12 +682,30 @@ hipError_t launch(KernelFn kern, const void* A, const void* B, void* C, int64_t 
 
 }  // namespace
 
+namespace {
+// Shape -> fastest variant, measured by the autotuner (software_pipelined_
+// tiled_pgemm_amd/autotune.py), which generates this file.
+const TunedShape kTuned[] = {
+#include "gemm_tuned.inc"
+};
+
+double log2_ratio(int64_t a, int64_t b) {
+    const double x = log2((double)(a > 0 ? a : 1)) - log2((double)(b > 0 ? b : 1));
+    return x < 0 ? -x : x;
+}
+}  // namespace
+
 int gemm_choose_variant(int64_t M, int64_t N, int64_t K) {
-    (void)K;
-    // Large tiles halve LDS traffic per MFMA; use them when they still give
-    // every CU (256 on MI355X) at least one tile.
-    const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    return big_tiles >= 256 ? kGemm256x256 : kGemm128x128;
+    int best = kGemm128x128;
+    double best_d = 1e300;
+    for (const TunedShape& t : kTuned) {
+        const double d = log2_ratio(M, t.M) + log2_ratio(N, t.N) + log2_ratio(K, t.K);
+        if (d < best_d) {
+            best_d = d;
+            best = t.variant;
+        }
+    }
+    return best;
 }
 
 hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N,

@@ -10,16 +10,23 @@ namespace pgemm {
 // GEMM tile configurations (ids match pgemm_f16_variant).
 enum GemmVariant : int {
     kGemmAuto = 0,
-    kGemm256x256 = 1,    // LDS-DMA pipeline, 4 stages of K 32
-    kGemm128x128 = 2,    // LDS-DMA pipeline, 4 stages of K 32
+    kGemm256x256 = 1,    // LDS-DMA pipeline, 5 stages of K 32
+    kGemm128x128 = 2,    // LDS-DMA pipeline, 5 stages of K 32
     kGemmRs256x256 = 3,  // register-staged pipeline, 2 LDS stages of K 64
     kGemmRs128x128 = 4,  // register-staged pipeline, 2 LDS stages of K 64
     kGemm256x256w8 = 5,  // LDS-DMA pipeline, 8 waves (2 per SIMD), 128x64 per wave
     kGemmNumVariants = 5,
 };
 
-// Picks a concrete variant for a problem shape.
+// Picks a concrete variant for a problem shape: the variant measured fastest
+// on the tuned shape nearest to (M, N, K) (gemm_tuned.inc, written by the
+// autotuner), distance = sum over M, N, K of |log2(shape / tuned shape)|.
 int gemm_choose_variant(int64_t M, int64_t N, int64_t K);
+
+struct TunedShape {
+    int64_t M, N, K;
+    int variant;
+};
 
 hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N,
                            int64_t K, int variant, hipStream_t stream);

@@ -71,6 +71,11 @@ int pgemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64
 
 int pgemm_f16_num_variants(void) { return pgemm::kGemmNumVariants; }
 
+int pgemm_f16_choose_variant(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return PGEMM_EINVAL;
+    return pgemm::gemm_choose_variant(M, N, K);
+}
+
 int pstream_add_blocked(const float* x, const float* y, float* z, int64_t n, int64_t block_elems,
                         pgemm_stream_t stream) {
     if (n < 0) return PGEMM_EINVAL;
