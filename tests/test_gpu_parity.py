@@ -365,7 +365,11 @@ def test_sum_axis0_pages_worked_example():
 
 
 @pytest.mark.parametrize("R,shape", [(8, (1024, 1024)), (1, (100,)), (3, (64, 33)), (9, (4096,)),
-                                     (17, (255, 4)), (1000, (64,)), (2, (1,)), (13, (7, 3))])
+                                     (17, (255, 4)), (1000, (64,)), (2, (1,)), (13, (7, 3)),
+                                     # 3 full blocks of 1024 float4 + a block with 300
+                                     (5, (3 * 4096 + 1200,)),
+                                     # the shape bench.py times
+                                     (8, (4096, 4096))])
 def test_sum_axis0_bit_exact_vs_oracle(R, shape):
     say("sum axis 0 R=%d shape=%s" % (R, shape))
     x = inputs.uniform_f32((R,) + shape, 60 + R)
