@@ -83,6 +83,9 @@ int pgemm_f16(const void* A, const void* B, void* C,
  *      quickstart's matmul)
  *   5  256x256 output tile, 8 waves (two per SIMD, 128x64 each), otherwise
  *      as 1
+ *   6  128x128 output tile, wave-specialised: 4 waves only read LDS and
+ *      multiply, a fifth wave issues every global->LDS copy and waits for
+ *      them (the pages' warp-specialised pipeline); ring and copy order as 2
  * Every variant gives bit-identical results for the same inputs (the K
  * order inside each output element depends neither on the tiling nor on
  * the pipeline).

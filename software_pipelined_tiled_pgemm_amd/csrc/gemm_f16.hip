@@ -348,26 +348,27 @@ __device__ __forceinline__ void read_unit(int u, const char* stage, int s, int w
 
 // One half-step: the FN x FM MFMAs on (fa, fb), j-major, with the operand
 // reads of the next half-step (into na, nb) placed one per MFMA slot from the
-// first slot on, and the half-step's H copies (copy(0) .. copy(H-1),
-// global->LDS) spread evenly over the slots (copy c after MFMA
-// (2c+1)*NS/(2H)).  sched_barrier pins the order, so every read has most of
+// first slot on, and NC copies (copy(0) .. copy(NC-1), global->LDS; NC = H
+// in the dm kernel, 0 for the MFMA waves of the wave-specialised one) spread
+// evenly over the slots (copy c after MFMA (2c+1)*NS/(2NC)).  sched_barrier pins the order, so every read has most of
 // a half-step to land before its first use and the copies issue in the
 // matrix unit's shadow.
-template <class TL, class CopyFn>
+template <class TL, int NC = TL::H, class CopyFn>
 __device__ __forceinline__ void half_step(floatx16 (&acc)[TL::FN][TL::FM], const half8 (&fa)[TL::FM],
                                           const half8 (&fb)[TL::FN], const char* rstage, int rs,
                                           half8 (&na)[TL::FM], half8 (&nb)[TL::FN], int wm, int wn,
                                           int lane, CopyFn copy) {
     constexpr int NR = TL::FM + TL::FN;  // read units
     constexpr int NS = TL::FM * TL::FN;  // MFMA slots
+    constexpr int ND = NC > 0 ? NC : 1;
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
         const int j = q / TL::FM, i = q % TL::FM;
         acc[j][i] = mfma(fb[j], fa[i], acc[j][i]);
         if (q < NR) read_unit<TL>(q, rstage, rs, wm, wn, lane, na, nb);
 #pragma unroll
-        for (int c = 0; c < TL::H; ++c)
-            if (q == (2 * c + 1) * NS / (2 * TL::H)) copy(c);
+        for (int c = 0; c < NC; ++c)
+            if (q == (2 * c + 1) * NS / (2 * ND)) copy(c);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -479,6 +480,181 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 }
 
 }  // namespace dm
+
+// ===========================================================================
+// Wave-specialised LDS-DMA pipeline: MFMA waves that only read LDS and
+// multiply, plus one copy wave that issues every global->LDS copy.
+// ===========================================================================
+//
+// The pages' warp-specialised pipeline (Pallas Mosaic GPU pipelining, the
+// emit_pipeline_warp_specialized variant in the guide's platform notes, and
+// the Chinese quickstart) gives memory transfers a warpgroup of their own so
+// the compute warpgroups never stall on issuing them.  On gfx950 every wave
+// of a kernel gets the same register allocation, so a copy wave costs as
+// many registers as an MFMA wave: it fits next to the 128x128 tile's four
+// MFMA waves (about 170 registers each; the copy wave shares SIMD 0 with
+// MFMA wave 0) but not next to the 256x256 ones.  Layout, ring, swizzles and
+// the order of the K steps are those of the dm kernel, so the results are
+// bit-identical to it.
+namespace ws {
+
+using dm::BK;
+using dm::STAGES;
+using dm::aswz;
+using dm::bswz;
+using dm::wrap5;
+
+// Copies of the whole workgroup: piece t of the A (B) stage is the dm
+// kernel's copy t % A_CP of wave t / A_CP (B likewise), same LDS place.
+template <class TL>
+struct Producer {
+    static constexpr int NW = TL::WM * TL::WN;  // MFMA waves
+    static constexpr int NA = NW * TL::A_CP;    // A copies per step
+    static constexpr int NB = NW * TL::B_CP;    // B copies per step
+    uint32_t a_off[NA];
+    int a_k[NA];
+    uint32_t b_off[NB];
+
+    __device__ __forceinline__ void init(int lane, int K, int N, int n0) {
+#pragma unroll
+        for (int t = 0; t < NA; ++t) {
+            const int p = t * 64 + lane;
+            const int row = p >> 2;
+            const int c = (p & 3) ^ aswz(row);
+            a_off[t] = (uint32_t)((row * K + c * 8) * 2);
+            a_k[t] = c * 8;
+        }
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+            const int p = t * 64 + lane;
+            const int row = p / (TL::B_ROW / 16);
+            const int c = (p % (TL::B_ROW / 16)) ^ bswz(row);
+            const int n = c * 8;
+            b_off[t] = (n0 + n < N) ? (uint32_t)((row * N + n) * 2) : kOOB;
+        }
+    }
+    // B of step s into ring slot `slot`.
+    __device__ __forceinline__ void b_step(const _Float16* B, int N, int K, int n0, int s,
+                                           uint32_t stage) const {
+        const int k0 = s * BK;
+        const int kv = min(BK, K - k0);
+        const u32x4 rb = rsrc_words(B + (int64_t)k0 * N + n0, ((int64_t)kv * N - n0) * 2);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) dma16(rb, b_off[t], stage + TL::A_BYTES + t * 1024);
+    }
+    // A of steps s and s+1 into stages sa and sb, the two halves of each
+    // 128-byte line back to back.
+    __device__ __forceinline__ void a_pairs(const _Float16* A, int M, int K, int m0, int s,
+                                            uint32_t sa, uint32_t sb) const {
+        const int rows_valid = min(TL::BM, M - m0);
+        const int k0 = s * BK, k1 = k0 + BK;
+        const u32x4 r0 = rsrc_words(A + (int64_t)m0 * K + k0, ((int64_t)rows_valid * K - k0) * 2);
+        const u32x4 r1 = rsrc_words(A + (int64_t)m0 * K + k1, ((int64_t)rows_valid * K - k1) * 2);
+#pragma unroll
+        for (int t = 0; t < NA; ++t) {
+            dma16(r0, (a_k[t] < K - k0) ? a_off[t] : kOOB, sa + t * 1024);
+            dma16(r1, (a_k[t] < K - k1) ? a_off[t] : kOOB, sb + t * 1024);
+        }
+    }
+};
+
+// Copy-wave schedule, per period of two K steps (kt even):
+//   S1: B of kt+3 and kt+4; wait for step kt+1; barrier 1 (MFMA waves are
+//       in the middle of step kt; slot of kt is released)
+//   S2: A pairs of (kt+4, kt+5); wait for step kt+2; barrier 2 (middle of
+//       step kt+1; slot of kt+1 released)
+// B of kt+3 goes to the slot of kt-2 (released a period earlier), B and A of
+// kt+4 to the slot of kt-1 (released at the previous barrier 2), A of kt+5 to
+// the slot of kt (released at barrier 1 just before).  The prologue issues B0,
+// A(0,1), B1, B2, A(2,3) (B3 comes with S1 of the first period).  Wait
+// counts: step kt+1's last copy (its B) is followed by 3NB+2NA copies at
+// barrier 1; step kt+2's last copy (an A pair's first half) by 2NB+2NA+1 at
+// barrier 2, waited to 2NB+2NA.
+template <class TL>
+__global__ __launch_bounds__(TL::T + 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
+            _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
+            int group_m) {
+    __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
+    using P = Producer<TL>;
+    constexpr int NA = P::NA, NB = P::NB;
+    static_assert(3 * NB + 2 * NA < 64, "vmcnt range");
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * TL::BM, n0 = tn * TL::BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nk = (K + BK - 1) / BK;
+    const uint32_t ring = lds_addr(smem);
+
+    if (wave == P::NW) {
+        // ---- copy wave ----
+        if (nk > 0) {
+            P pr;
+            pr.init(lane, K, N, n0);
+            pr.b_step(B, N, K, n0, 0, ring);
+            pr.a_pairs(A, M, K, m0, 0, ring, ring + TL::STAGE);
+            pr.b_step(B, N, K, n0, 1, ring + TL::STAGE);
+            pr.b_step(B, N, K, n0, 2, ring + 2 * TL::STAGE);
+            pr.a_pairs(A, M, K, m0, 2, ring + 2 * TL::STAGE, ring + 3 * TL::STAGE);
+            wait_vmcnt<2 * NB + 2 * NA>();  // step 0 landed
+            __syncthreads();
+            int se = 0;
+            for (int kt = 0; kt < nk; kt += 2) {
+                const int s2 = wrap5(se + 2), s3 = wrap5(se + 3), s4 = wrap5(se + 4);
+                pr.b_step(B, N, K, n0, kt + 3, ring + s3 * TL::STAGE);
+                pr.b_step(B, N, K, n0, kt + 4, ring + s4 * TL::STAGE);
+                wait_vmcnt<3 * NB + 2 * NA>();  // step kt+1 landed
+                __syncthreads();
+                pr.a_pairs(A, M, K, m0, kt + 4, ring + s4 * TL::STAGE, ring + se * TL::STAGE);
+                wait_vmcnt<2 * NB + 2 * NA>();  // step kt+2 landed
+                __syncthreads();
+                se = s2;
+            }
+            wait_vmcnt<0>();  // the copies past the end of K
+        }
+        __syncthreads();  // matches the MFMA waves' barrier before the drain
+        __syncthreads();  // and the one inside the drain
+        return;
+    }
+
+    // ---- MFMA waves ----
+    const int wm = wave / TL::WN, wn = wave % TL::WN;
+    floatx16 acc[TL::FN][TL::FM];
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j)
+#pragma unroll
+        for (int i = 0; i < TL::FM; ++i) acc[j][i] = floatx16{};
+    if (nk > 0) {
+        __syncthreads();  // step 0 landed
+        half8 fa[2][TL::FM], fb[2][TL::FN];
+#pragma unroll
+        for (int u = 0; u < TL::FM + TL::FN; ++u)
+            dm::read_unit<TL>(u, smem, 0, wm, wn, lane, fa[0], fb[0]);
+        auto none = [](int) {};
+        int se = 0;
+        for (int kt = 0; kt < nk; kt += 2) {
+            const int s1 = wrap5(se + 1), s2 = wrap5(se + 2);
+            const char* cur = smem + se * TL::STAGE;
+            const char* nxt = smem + s1 * TL::STAGE;
+            dm::half_step<TL, 0>(acc, fa[0], fb[0], cur, 1, fa[1], fb[1], wm, wn, lane, none);
+            __syncthreads();  // step kt+1 landed; slot se released
+            dm::half_step<TL, 0>(acc, fa[1], fb[1], nxt, 0, fa[0], fb[0], wm, wn, lane, none);
+            dm::half_step<TL, 0>(acc, fa[0], fb[0], nxt, 1, fa[1], fb[1], wm, wn, lane, none);
+            __syncthreads();  // step kt+2 landed; slot s1 released
+            dm::half_step<TL, 0>(acc, fa[1], fb[1], smem + s2 * TL::STAGE, 0, fa[0], fb[0], wm, wn,
+                                 lane, none);
+            se = s2;
+        }
+    }
+    __syncthreads();  // every wave is done with the stage ring
+    drain<TL::BM, TL::BN, TL::TM, TL::TN, TL::FM, TL::FN, TL::T>(smem, acc, C, M, N, m0, n0, tid,
+                                                                 wm, wn);
+}
+
+}  // namespace ws
 
 // ===========================================================================
 // Register-staged pipeline: 2 LDS stages of BK = 64 plus a register stage.
@@ -667,14 +843,14 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 
 template <class TL, class KernelFn>
 hipError_t launch(KernelFn kern, const void* A, const void* B, void* C, int64_t M, int64_t N,
-                  int64_t K, hipStream_t stream) {
+                  int64_t K, hipStream_t stream, int threads = TL::T) {
     const int tiles_m = (int)((M + TL::BM - 1) / TL::BM);
     const int tiles_n = (int)((N + TL::BN - 1) / TL::BN);
     const int nwg = tiles_m * tiles_n;
     // Bands of 4 tile rows: a run of consecutive logical tiles then covers
     // 4 rows x (run/4) columns of tiles.
     const int group_m = tiles_m < 4 ? tiles_m : 4;
-    hipLaunchKernelGGL(kern, dim3(nwg), dim3(TL::T), 0, stream, static_cast<const _Float16*>(A),
+    hipLaunchKernelGGL(kern, dim3(nwg), dim3(threads), 0, stream, static_cast<const _Float16*>(A),
                        static_cast<const _Float16*>(B), static_cast<_Float16*>(C), (int)M, (int)N,
                        (int)K, tiles_m, tiles_n, group_m);
     return hipGetLastError();
@@ -723,6 +899,10 @@ hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int
         case kGemm256x256w8: {
             using TL = dm::Tile<256, 256, 2, 4>;
             return launch<TL>(dm::kernel<TL, 2>, A, B, C, M, N, K, stream);
+        }
+        case kGemmWs128x128: {
+            using TL = dm::Tile<128, 128>;
+            return launch<TL>(ws::kernel<TL>, A, B, C, M, N, K, stream, TL::T + 64);
         }
         case kGemmRs256x256: {
             using TL = rs::Tile<256, 256>;

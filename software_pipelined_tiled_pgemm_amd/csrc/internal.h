@@ -15,7 +15,8 @@ enum GemmVariant : int {
     kGemmRs256x256 = 3,  // register-staged pipeline, 2 LDS stages of K 64
     kGemmRs128x128 = 4,  // register-staged pipeline, 2 LDS stages of K 64
     kGemm256x256w8 = 5,  // LDS-DMA pipeline, 8 waves (2 per SIMD), 128x64 per wave
-    kGemmNumVariants = 5,
+    kGemmWs128x128 = 6,  // wave-specialised LDS-DMA pipeline: 4 MFMA waves + 1 copy wave
+    kGemmNumVariants = 6,
 };
 
 // Picks a concrete variant for a problem shape: the variant measured fastest

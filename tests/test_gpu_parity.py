@@ -68,7 +68,7 @@ def bits_equal(a, b):
     return np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-VARIANTS = [1, 2, 3, 4, 5]
+VARIANTS = [1, 2, 3, 4, 5, 6]
 
 
 # ------------------------------------------------------------ worked examples
