@@ -7,10 +7,10 @@
 // and it is written out once after the last step.  Here the output block of
 // a lane is U float4s held in registers (lane-interleaved, so one wave reads
 // U KiB contiguous of every slice); the R slices it reads are the pipeline's
-// steps.  A register ring (the guide's section 4 multi-buffering, kRing
-// slots) keeps the loads of the next slices in flight while the current one
-// is added: copy_start early, copy_wait (the compiler's vmcnt wait) just
-// before the add.  The adds happen in ascending slice order, one IEEE
+// steps.  The register ring of pipeline.h (the guide's section 4
+// multi-buffering, kRing slots) keeps the loads of the next slices in flight
+// while the current one is added: copy_start early, copy_wait (the
+// compiler's vmcnt wait) just before the add.  The adds happen in ascending slice order, one IEEE
 // binary32 addition per slice, starting from +0.0f, so the result is
 // bit-identical to the plain sequential loop.
 //
@@ -23,6 +23,7 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "pipeline.h"
 
 namespace pgemm {
 namespace {
@@ -47,31 +48,21 @@ __global__ __launch_bounds__(kThreads) void sum_axis0_vec_kernel(const float* x,
         in[u] = base + u * kThreads < lanes;
         acc[u] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};  // zero-init at the first step
     }
-    floatx4 ring[kRing][kUnroll];
+    struct Slice {
+        floatx4 v[kUnroll];
+    };
+    ring_pipeline<kRing, Slice>(
+        R,
+        [&](int64_t s, Slice& sl) {  // copy_start of slice s
 #pragma unroll
-    for (int s = 0; s < kRing; ++s)  // prologue: copy_start for slices 0 .. kRing-1
+            for (int u = 0; u < kUnroll; ++u)
+                sl.v[u] = in[u] ? __builtin_nontemporal_load(src + s * lanes + base + u * kThreads)
+                                : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        },
+        [&](int64_t, const Slice& sl) {  // slices arrive in ascending order
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            if (s < R && in[u])
-                ring[s][u] = __builtin_nontemporal_load(src + s * lanes + base + u * kThreads);
-    int64_t i = 0;
-    for (; i + kRing <= R; i += kRing) {
-#pragma unroll
-        for (int s = 0; s < kRing; ++s) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                acc[u] += ring[s][u];  // slice i+s: copy_wait, then the add
-                if (i + s + kRing < R && in[u])
-                    ring[s][u] = __builtin_nontemporal_load(src + (i + s + kRing) * lanes + base +
-                                                            u * kThreads);
-            }
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < kRing; ++s)
-        if (i + s < R)
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) acc[u] += ring[s][u];
+            for (int u = 0; u < kUnroll; ++u) acc[u] += sl.v[u];
+        });
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
         if (in[u])

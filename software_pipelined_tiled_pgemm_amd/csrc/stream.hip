@@ -9,19 +9,23 @@
 // spaces": ALU-only work bypasses shared memory).  The kernel is bound by HBM
 // bandwidth: 12 bytes move per element for x + y, 8 for x + c.
 //
-// Each lane issues all of its 16-byte loads for an unrolled group before any
-// add (copy_start early), adds once the data is back (copy_wait late) and
-// stores; the loads of other workgroups overlap those stores.  With the
-// default block (4096 elements for x + y, 8192 for x + c) every lane does
-// exactly one such group.  Loads and stores are non-temporal: the data is
-// touched once, so it should not displace anything in the caches.
-// Arithmetic is one IEEE binary32 add per element (v_add_f32, RNE, denormals
-// kept), so results are bit-identical to any IEEE implementation.
+// Inside a workgroup's block each lane walks groups of kUnroll 16-byte
+// pieces per operand through a register ring (pipeline.h, the guide's
+// section 4 pipeline with kStages buffers): the loads of the next groups are
+// in flight while the current group is added and stored.  With the default
+// block (4096 elements for x + y, 8192 for x + c) every lane has exactly one
+// group and the overlap comes from the many workgroups; with the pages'
+// 512 x 512 blocks (one workgroup per CU) the ring is what keeps enough
+// bytes in flight.  Loads and stores are non-temporal: the data is touched
+// once, so it should not displace anything in the caches.  Arithmetic is one
+// IEEE binary32 add per element (v_add_f32, RNE, denormals kept), so results
+// are bit-identical to any IEEE implementation.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "internal.h"
+#include "pipeline.h"
 
 namespace pgemm {
 namespace {
@@ -29,11 +33,24 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;  // 16-byte loads in flight per operand per lane
+constexpr int kUnroll = 4;  // 16-byte loads per operand per lane and group
+#ifndef PGEMM_STREAM_STAGES
+#define PGEMM_STREAM_STAGES 2
+#endif
+// Groups in flight per lane: 2 is the guide's double buffer.  Depths 1 to 4
+// measured the same on MI355X (5.7-5.9 TB/s at the pages' 512x512 blocks,
+// 6.6 TB/s at the default block), so the smallest register footprint wins.
+constexpr int kStages = PGEMM_STREAM_STAGES;
+
+struct AddSlot {
+    floatx4 a[kUnroll], b[kUnroll];
+};
 
 // One workgroup per block of `block` elements (block is a multiple of 1024,
-// so a block starts 16-byte aligned whenever the arrays do).  The last block
-// may be ragged; its scalar tail is handled by the same workgroup.
+// so a block starts 16-byte aligned whenever the arrays do).  Group g of a
+// block is float4s g*kUnroll*kThreads .. +kUnroll*kThreads-1, lane t taking
+// every kThreads-th.  The last block may be ragged: its whole float4s past
+// the last full group and its scalar tail are handled by the same workgroup.
 __global__ __launch_bounds__(kThreads) void add_vec_kernel(const float* x, const float* y,
                                                            float* z, int64_t n, int64_t block) {
     const int64_t start = (int64_t)blockIdx.x * block;
@@ -42,21 +59,25 @@ __global__ __launch_bounds__(kThreads) void add_vec_kernel(const float* x, const
     const floatx4* xv = reinterpret_cast<const floatx4*>(x + start);
     const floatx4* yv = reinterpret_cast<const floatx4*>(y + start);
     floatx4* zv = reinterpret_cast<floatx4*>(z + start);
-
-    int64_t i = threadIdx.x;
-    for (; i + (kUnroll - 1) * kThreads < nv; i += kUnroll * kThreads) {
-        floatx4 a[kUnroll], b[kUnroll];
+    constexpr int64_t G = (int64_t)kUnroll * kThreads;
+    const int64_t groups = nv / G;
+    const int t = threadIdx.x;
+    ring_pipeline<kStages, AddSlot>(
+        groups,
+        [&](int64_t g, AddSlot& sl) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            a[u] = __builtin_nontemporal_load(xv + i + u * kThreads);
-            b[u] = __builtin_nontemporal_load(yv + i + u * kThreads);
-        }
+            for (int u = 0; u < kUnroll; ++u) {
+                sl.a[u] = __builtin_nontemporal_load(xv + g * G + u * kThreads + t);
+                sl.b[u] = __builtin_nontemporal_load(yv + g * G + u * kThreads + t);
+            }
+        },
+        [&](int64_t g, const AddSlot& sl) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(a[u] + b[u], zv + i + u * kThreads);
-    }
-    for (; i < nv; i += kThreads) zv[i] = xv[i] + yv[i];
-    for (int64_t e = (nv << 2) + threadIdx.x; e < len; e += kThreads)
-        z[start + e] = x[start + e] + y[start + e];
+            for (int u = 0; u < kUnroll; ++u)
+                __builtin_nontemporal_store(sl.a[u] + sl.b[u], zv + g * G + u * kThreads + t);
+        });
+    for (int64_t i = groups * G + t; i < nv; i += kThreads) zv[i] = xv[i] + yv[i];
+    for (int64_t e = (nv << 2) + t; e < len; e += kThreads) z[start + e] = x[start + e] + y[start + e];
 }
 
 // Any alignment: one element per lane per iteration.
@@ -67,6 +88,12 @@ __global__ __launch_bounds__(kThreads) void add_scalar_path_kernel(const float* 
         z[i] = x[i] + y[i];
 }
 
+struct AddcSlot {
+    floatx4 a[2 * kUnroll];
+};
+
+// x + c: one input, so twice the float4s per group for the same bytes in
+// flight.
 __global__ __launch_bounds__(kThreads) void addc_vec_kernel(const float* x, float c, float* z,
                                                             int64_t n, int64_t block) {
     const int64_t start = (int64_t)blockIdx.x * block;
@@ -74,18 +101,23 @@ __global__ __launch_bounds__(kThreads) void addc_vec_kernel(const float* x, floa
     const int64_t nv = len >> 2;
     const floatx4* xv = reinterpret_cast<const floatx4*>(x + start);
     floatx4* zv = reinterpret_cast<floatx4*>(z + start);
-
-    int64_t i = threadIdx.x;
-    for (; i + (2 * kUnroll - 1) * kThreads < nv; i += 2 * kUnroll * kThreads) {
-        floatx4 a[2 * kUnroll];
+    constexpr int64_t G = (int64_t)2 * kUnroll * kThreads;
+    const int64_t groups = nv / G;
+    const int t = threadIdx.x;
+    ring_pipeline<kStages, AddcSlot>(
+        groups,
+        [&](int64_t g, AddcSlot& sl) {
 #pragma unroll
-        for (int u = 0; u < 2 * kUnroll; ++u) a[u] = __builtin_nontemporal_load(xv + i + u * kThreads);
+            for (int u = 0; u < 2 * kUnroll; ++u)
+                sl.a[u] = __builtin_nontemporal_load(xv + g * G + u * kThreads + t);
+        },
+        [&](int64_t g, const AddcSlot& sl) {
 #pragma unroll
-        for (int u = 0; u < 2 * kUnroll; ++u) __builtin_nontemporal_store(a[u] + c, zv + i + u * kThreads);
-    }
-    for (; i < nv; i += kThreads) zv[i] = xv[i] + c;
-    for (int64_t e = (nv << 2) + threadIdx.x; e < len; e += kThreads)
-        z[start + e] = x[start + e] + c;
+            for (int u = 0; u < 2 * kUnroll; ++u)
+                __builtin_nontemporal_store(sl.a[u] + c, zv + g * G + u * kThreads + t);
+        });
+    for (int64_t i = groups * G + t; i < nv; i += kThreads) zv[i] = xv[i] + c;
+    for (int64_t e = (nv << 2) + t; e < len; e += kThreads) z[start + e] = x[start + e] + c;
 }
 
 __global__ __launch_bounds__(kThreads) void addc_scalar_path_kernel(const float* x, float c,
