@@ -119,17 +119,29 @@ def time_launches(fn, steps, warmup, stream):
     return start.elapsed_time(end) / 1e3  # seconds
 
 
-def gemm_case(pg, inputs, M, N, K, dist, steps, warmup, stream):
+def gemm_case(pg, inputs, M, N, K, dist, steps, warmup, stream, splitk=False):
     import torch
     A, B = inputs.gemm_inputs(M, N, K, dist)
     tA = torch.from_numpy(A).cuda()
     tB = torch.from_numpy(B).cuda()
     tC = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    secs = time_launches(lambda i: pg.pgemm_f16(tA, tB, C=tC), steps, warmup, stream)
+    rec = {"M": M, "N": N, "K": K, "dist": dist}
+    if splitk:
+        splits = pg.pgemm_f16_splitk_default_splits(M, N, K)
+        ws = torch.empty(max(pg.pgemm_f16_splitk_workspace_bytes(M, N, K, splits) // 4, 1),
+                         dtype=torch.float32, device="cuda")
+        fn = lambda i: pg.pgemm_f16_splitk(tA, tB, splits, C=tC, workspace=ws)
+        rec["path"] = "pgemm_f16_splitk, %d splits, %d MiB fp32 workspace" % (
+            splits, ws.numel() * 4 >> 20)
+    else:
+        fn = lambda i: pg.pgemm_f16(tA, tB, C=tC)
+        rec["path"] = "pgemm_f16 (variant %d)" % pg.pgemm_f16_choose_variant(M, N, K)
+    secs = time_launches(fn, steps, warmup, stream)
     flops = 2.0 * M * N * K
     tflops = flops * steps / secs / 1e12
-    return {"M": M, "N": N, "K": K, "dist": dist, "us_per_launch": secs / steps * 1e6,
-            "tflops": tflops, "frac_of_peak": tflops / PEAK_FP16_TFLOPS}
+    rec.update({"us_per_launch": secs / steps * 1e6, "tflops": tflops,
+                "frac_of_peak": tflops / PEAK_FP16_TFLOPS})
+    return rec
 
 
 def stream_case(pg, inputs, steps, warmup, stream, scalar):
@@ -275,6 +287,12 @@ def main():
             print("gemm %dx%dx%d: %.1f us, %.1f TFLOP/s" % (M, N, K, r["us_per_launch"], r["tflops"]),
                   file=sys.stderr, flush=True)
             others.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+        # long K through split-K (the caller provides the fp32 workspace)
+        r = gemm_case(pg, inputs, 2048, 2048, 32768, "uniform", max(5, args.steps // 10),
+                      max(3, args.warmup // 10), stream, splitk=True)
+        print("gemm 2048x2048x32768 split-K: %.1f us, %.1f TFLOP/s" % (r["us_per_launch"], r["tflops"]),
+              file=sys.stderr, flush=True)
+        others.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         out["other_gemm"] = others
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds)

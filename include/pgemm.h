@@ -99,6 +99,44 @@ int pgemm_f16_variant(const void* A, const void* B, void* C,
 int pgemm_f16_num_variants(void);
 
 /*
+ * Split-K GEMM for shapes with few output tiles and a long K (the pages'
+ * parallel grid has only the output tiles to spread over the CUs, so a long
+ * K leaves most CUs idle or forces small tiles).  K is cut into
+ * P = pgemm's number of chunks of ceil(K/splits) rounded up to a multiple of
+ * 64; chunk p runs as its own workgroups, multiplying A[:, chunk] by
+ * B[chunk, :] with fp32 accumulation into the fp32 partial
+ * workspace[p*M*N .. (p+1)*M*N) (row-major, pitch N); a second kernel then
+ * writes C = fp16_rne(W_0 + W_1 + ... + W_{P-1}), the partials added in
+ * ascending p in fp32.  Deterministic, within the same error bound as
+ * pgemm_f16 but not bit-identical to it (another summation order), except
+ * when P == 1: then it is exactly pgemm_f16 and needs no workspace.
+ *   splits     requested number of chunks, 1 .. 64
+ *   workspace  device memory of at least
+ *              pgemm_f16_splitk_workspace_bytes(M, N, K, splits) bytes,
+ *              16-byte aligned, disjoint from A, B and C; owned by the
+ *              caller, contents overwritten, free to reuse once the stream
+ *              has passed this call
+ * Other arguments and requirements as pgemm_f16.  Returns PGEMM_EINVAL for a
+ * missing, too small or overlapping workspace, PGEMM_EUNSUPPORTED for splits
+ * out of range, a misaligned workspace or M*N > 2^36, else as pgemm_f16.
+ */
+int pgemm_f16_splitk(const void* A, const void* B, void* C,
+                     int64_t M, int64_t N, int64_t K, int splits,
+                     void* workspace, int64_t workspace_bytes,
+                     pgemm_stream_t stream);
+
+/* Workspace bytes pgemm_f16_splitk needs (0 when K forms a single chunk);
+ * PGEMM_EINVAL / PGEMM_EUNSUPPORTED (negative) on invalid arguments. */
+int64_t pgemm_f16_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splits);
+
+/* A split count for pgemm_f16_splitk measured to pay off on MI355X: enough
+ * (256x256 output tile, K chunk) pairs to give each of the 256 CUs one, with
+ * chunks of at least 4096 and at most 8 splits; 1 (no split) when the output
+ * alone has 256 tiles or K is short.  Pure host function.  PGEMM_EINVAL for a
+ * negative size. */
+int pgemm_f16_splitk_default_splits(int64_t M, int64_t N, int64_t K);
+
+/*
  * The variant (1 .. pgemm_f16_num_variants()) that pgemm_f16 uses for an
  * M x N x K problem: the fastest variant on the nearest shape of the tuned
  * table built into the library.  The table is written by the autotuner

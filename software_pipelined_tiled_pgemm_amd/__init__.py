@@ -14,6 +14,7 @@ from ._lib import (PGEMM_EHIP, PGEMM_EINVAL, PGEMM_EUNSUPPORTED, PGEMM_OK, Pgemm
 
 __all__ = [
     "pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants", "pgemm_f16_choose_variant",
+    "pgemm_f16_splitk", "pgemm_f16_splitk_workspace_bytes", "pgemm_f16_splitk_default_splits",
     "pstream_add", "pstream_add_blocked", "pstream_add_scalar", "preduce_sum_f32",
     "pgemm_test_fill_f32", "pgemm_test_iota_f32",
     "lib", "status_string", "PgemmError",
@@ -77,6 +78,53 @@ def pgemm_f16_variant(A, B, variant, C=None, stream=None):
         rc = lib().pgemm_f16_variant(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K,
                                      int(variant), _stream_handle(A.device, stream))
     _call(rc, "pgemm_f16")
+    return C
+
+
+def pgemm_f16_splitk_workspace_bytes(M, N, K, splits):
+    rc = lib().pgemm_f16_splitk_workspace_bytes(int(M), int(N), int(K), int(splits))
+    if rc < 0:
+        raise PgemmError(int(rc), "pgemm_f16_splitk_workspace_bytes")
+    return rc
+
+
+def pgemm_f16_splitk_default_splits(M, N, K):
+    rc = lib().pgemm_f16_splitk_default_splits(int(M), int(N), int(K))
+    if rc < 0:
+        raise PgemmError(rc, "pgemm_f16_splitk_default_splits")
+    return rc
+
+
+def pgemm_f16_splitk(A, B, splits=None, C=None, workspace=None, stream=None):
+    """C = A @ B with K cut into `splits` chunks (None: the library's default
+    for the shape) reduced through an fp32 workspace (allocated here with
+    torch when not given)."""
+    torch = _torch()
+    _check_dev(A, torch.float16, "A", 2)
+    _check_dev(B, torch.float16, "B", 2)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2 or A.device != B.device:
+        raise ValueError("inner dimensions or devices differ")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    else:
+        _check_dev(C, torch.float16, "C", 2)
+        if tuple(C.shape) != (M, N) or C.device != A.device:
+            raise ValueError("C must be a (%d, %d) tensor on %s" % (M, N, A.device))
+    if splits is None:
+        splits = pgemm_f16_splitk_default_splits(M, N, K)
+    need = pgemm_f16_splitk_workspace_bytes(M, N, K, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=A.device)
+    elif workspace.device != A.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % A.device)
+    with torch.cuda.device(A.device):
+        rc = lib().pgemm_f16_splitk(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, int(splits),
+                                    workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream_handle(A.device, stream))
+    _call(rc, "pgemm_f16_splitk")
     return C
 
 

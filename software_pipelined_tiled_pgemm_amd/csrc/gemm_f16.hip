@@ -53,6 +53,7 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(8)));
@@ -198,6 +199,53 @@ __device__ __forceinline__ void drain(char* smem, floatx16 (&acc)[FN][FM], _Floa
     }
 }
 
+// Split-K drain: the fp32 partial tile to row-major fp32 (pitch N) at W,
+// through LDS one band of wave rows (TM rows) at a time: the waves of band r
+// write their blocks (lane (lr, lk) of block (j, i) holds 4 consecutive
+// columns of one row), then every thread stores 16-byte row chunks.  The
+// 16-byte chunk c of LDS row r sits at c ^ (r mod chunks-per-row).
+template <int BN, int TM, int TN, int FM, int FN, int T, int WM>
+__device__ __forceinline__ void drain_f32(char* smem, floatx16 (&acc)[FN][FM], float* W, int M,
+                                          int N, int m0, int n0, int tid, int wm, int wn) {
+    constexpr int CH = BN / 4;     // 16-byte chunks per fp32 row
+    constexpr int ROWB = BN * 4;   // bytes per LDS row
+    constexpr int RSTEP = T / CH;  // rows per store pass
+    static_assert(TM % RSTEP == 0, "store passes cover the band");
+    const int lane = tid & 63;
+    const int lr = lane & 31, lk = lane >> 5;
+    const int chunk = tid % CH, row0 = tid / CH;
+    const bool col_ok = n0 + chunk * 4 < N;
+#pragma unroll
+    for (int r = 0; r < WM; ++r) {
+        if (wm == r) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int row = i * 32 + lr;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int c = (wn * TN + j * 32) / 4 + 2 * g + lk;
+                        const floatx4 v = {acc[j][i][4 * g + 0], acc[j][i][4 * g + 1],
+                                           acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]};
+                        *reinterpret_cast<floatx4*>(smem + row * ROWB + (c ^ (row & (CH - 1))) * 16) = v;
+                    }
+                }
+        }
+        __syncthreads();
+        const int grow0 = m0 + r * TM;
+#pragma unroll
+        for (int q = 0; q < TM / RSTEP; ++q) {
+            const int row = row0 + RSTEP * q;
+            const floatx4 v =
+                *reinterpret_cast<const floatx4*>(smem + row * ROWB + (chunk ^ (row & (CH - 1))) * 16);
+            if (col_ok && grow0 + row < M)
+                *reinterpret_cast<floatx4*>(W + (int64_t)(grow0 + row) * N + n0 + chunk * 4) = v;
+        }
+        __syncthreads();
+    }
+}
+
 // ===========================================================================
 // LDS-DMA pipeline: 5-stage LDS ring, BK = 32, copies straight into LDS.
 // ===========================================================================
@@ -271,14 +319,16 @@ struct Copier {
     uint32_t a_off[TL::A_CP];
     int a_k[TL::A_CP];
     uint32_t b_off[TL::B_CP];
+    int lda;  // row pitch of A in elements (K, or the full K of a K-chunk view)
 
-    __device__ __forceinline__ void init(int lane, int wave, int K, int N, int n0) {
+    __device__ __forceinline__ void init(int lane, int wave, int lda_, int N, int n0) {
+        lda = lda_;
 #pragma unroll
         for (int t = 0; t < TL::A_CP; ++t) {
             const int p = (wave * TL::A_CP + t) * 64 + lane;  // 16-byte chunk in the A stage
             const int row = p >> 2;
             const int c = (p & 3) ^ aswz(row);
-            a_off[t] = (uint32_t)((row * K + c * 8) * 2);
+            a_off[t] = (uint32_t)((row * lda + c * 8) * 2);
             a_k[t] = c * 8;
         }
 #pragma unroll
@@ -290,11 +340,13 @@ struct Copier {
             b_off[t] = (n0 + n < N) ? (uint32_t)((row * N + n) * 2) : kOOB;
         }
     }
-    // A copy t of step k0 into the stage at LDS byte address `stage`.
+    // A copy t of step k0 into the stage at LDS byte address `stage`; K is
+    // the extent (pieces at K and beyond read as zeros), lda the row pitch.
     __device__ __forceinline__ void issue_a(int t, const _Float16* A, int M, int K, int m0, int k0,
                                             uint32_t stage, int wave) const {
         const int rows_valid = min(TL::BM, M - m0);
-        const u32x4 ra = rsrc_words(A + (int64_t)m0 * K + k0, ((int64_t)rows_valid * K - k0) * 2);
+        const u32x4 ra =
+            rsrc_words(A + (int64_t)m0 * lda + k0, ((int64_t)rows_valid * lda - k0) * 2);
         const uint32_t off = (a_k[t] < K - k0) ? a_off[t] : kOOB;
         dma16(ra, off, stage + (wave * TL::A_CP + t) * 1024);
     }
@@ -387,13 +439,27 @@ __device__ __forceinline__ int wrap5(int s) { return s >= STAGES ? s - STAGES : 
 // kt, so every copy lands in a released slot.  The wait in the middle of step
 // kt covers step kt+1: for kt even its last copy (B) is 5H copies old, for kt
 // odd its last copy (an A pair's first half) is 4H+1 old.
-template <class TL, int WPE>
+//
+// SPLIT (split-K): blockIdx.y = s takes the K chunk [s*chunk, s*chunk +
+// chunk) as a sub-matrix view (A shifted by s*chunk columns with its full row
+// pitch, B by s*chunk rows) and writes its fp32 partial product to
+// W + s*M*N instead of rounding to C.
+template <class TL, int WPE, bool SPLIT = false>
 __global__ __launch_bounds__(TL::T, 1) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
-            _Float16* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
-            int group_m) {
+void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
+            _Float16* __restrict__ C, int M, int N, int Kfull, int tiles_m, int tiles_n,
+            int group_m, float* __restrict__ W, int chunk) {
     __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
     constexpr int H = TL::H;
+    const _Float16* A = A0;
+    const _Float16* B = B0;
+    int K = Kfull;  // extent of this workgroup's K range
+    if constexpr (SPLIT) {
+        const int kb = blockIdx.y * chunk;
+        K = min(chunk, Kfull - kb);
+        A = A0 + kb;
+        B = B0 + (int64_t)kb * N;
+    }
 
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
@@ -412,7 +478,7 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     const int nk = (K + BK - 1) / BK;
     if (nk > 0) {
         Copier<TL> cp;
-        cp.init(lane, wave, K, N, n0);
+        cp.init(lane, wave, Kfull, N, n0);
         const uint32_t ring = lds_addr(smem);
         // A pairs t0 .. t0+A_CP/2-1 of steps (s, s+1) into slots (sa, sb).
         auto a_pairs = [&](int q, int t0, int s, int sa, int sb) __attribute__((always_inline)) {
@@ -475,8 +541,12 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
         wait_vmcnt<0>();  // drain the copies of the steps past the end
     }
     __syncthreads();  // every wave is done with the stage ring
-    drain<TL::BM, TL::BN, TL::TM, TL::TN, TL::FM, TL::FN, TL::T>(smem, acc, C, M, N, m0, n0, tid,
-                                                                 wm, wn);
+    if constexpr (SPLIT)
+        drain_f32<TL::BN, TL::TM, TL::TN, TL::FM, TL::FN, TL::T, TL::WM>(
+            smem, acc, W + (int64_t)blockIdx.y * M * N, M, N, m0, n0, tid, wm, wn);
+    else
+        drain<TL::BM, TL::BN, TL::TM, TL::TN, TL::FM, TL::FN, TL::T>(smem, acc, C, M, N, m0, n0,
+                                                                     tid, wm, wn);
 }
 
 }  // namespace dm
@@ -841,21 +911,21 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
 
 }  // namespace rs
 
-template <class TL, class KernelFn>
-hipError_t launch(KernelFn kern, const void* A, const void* B, void* C, int64_t M, int64_t N,
-                  int64_t K, hipStream_t stream, int threads = TL::T) {
+template <class TL, class KernelFn, class... Extra>
+hipError_t launch(KernelFn kern, int threads, int splits, const void* A, const void* B, void* C,
+                  int64_t M, int64_t N, int64_t K, hipStream_t stream, Extra... extra) {
     const int tiles_m = (int)((M + TL::BM - 1) / TL::BM);
     const int tiles_n = (int)((N + TL::BN - 1) / TL::BN);
     const int nwg = tiles_m * tiles_n;
     // Bands of 4 tile rows: a run of consecutive logical tiles then covers
     // 4 rows x (run/4) columns of tiles.
     const int group_m = tiles_m < 4 ? tiles_m : 4;
-    hipLaunchKernelGGL(kern, dim3(nwg), dim3(threads), 0, stream, static_cast<const _Float16*>(A),
-                       static_cast<const _Float16*>(B), static_cast<_Float16*>(C), (int)M, (int)N,
-                       (int)K, tiles_m, tiles_n, group_m);
+    hipLaunchKernelGGL(kern, dim3(nwg, splits), dim3(threads), 0, stream,
+                       static_cast<const _Float16*>(A), static_cast<const _Float16*>(B),
+                       static_cast<_Float16*>(C), (int)M, (int)N, (int)K, tiles_m, tiles_n, group_m,
+                       extra...);
     return hipGetLastError();
 }
-
 }  // namespace
 
 namespace {
@@ -884,33 +954,54 @@ int gemm_choose_variant(int64_t M, int64_t N, int64_t K) {
     return best;
 }
 
+hipError_t launch_gemm_f16_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                                  int64_t K, int64_t chunk, int splits, float* W,
+                                  hipStream_t stream) {
+    // 256x256 tiles (8 waves) when the (tile, chunk) pairs fill the chip's
+    // 256 CUs, 128x128 otherwise.
+    const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+    hipError_t rc;
+    if (big * splits >= 256) {
+        using TL = dm::Tile<256, 256, 2, 4>;
+        rc = launch<TL>(dm::kernel<TL, 2, true>, TL::T, splits, A, B, C, M, N, K, stream, W,
+                        (int)chunk);
+    } else {
+        using TL = dm::Tile<128, 128>;
+        rc = launch<TL>(dm::kernel<TL, 2, true>, TL::T, splits, A, B, C, M, N, K, stream, W,
+                        (int)chunk);
+    }
+    if (rc != hipSuccess) return rc;
+    return launch_splitk_sum(W, static_cast<_Float16*>(C), splits, M * N, stream);
+}
+
 hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N,
                            int64_t K, int variant, hipStream_t stream) {
     if (variant == kGemmAuto) variant = gemm_choose_variant(M, N, K);
+    float* const nows = nullptr;  // no split-K workspace
     switch (variant) {
         case kGemm256x256: {
             using TL = dm::Tile<256, 256>;
-            return launch<TL>(dm::kernel<TL, 1>, A, B, C, M, N, K, stream);
+            return launch<TL>(dm::kernel<TL, 1>, TL::T, 1, A, B, C, M, N, K, stream, nows, 0);
         }
         case kGemm128x128: {
             using TL = dm::Tile<128, 128>;
-            return launch<TL>(dm::kernel<TL, 2>, A, B, C, M, N, K, stream);
+            return launch<TL>(dm::kernel<TL, 2>, TL::T, 1, A, B, C, M, N, K, stream, nows, 0);
         }
         case kGemm256x256w8: {
             using TL = dm::Tile<256, 256, 2, 4>;
-            return launch<TL>(dm::kernel<TL, 2>, A, B, C, M, N, K, stream);
+            return launch<TL>(dm::kernel<TL, 2>, TL::T, 1, A, B, C, M, N, K, stream, nows, 0);
         }
         case kGemmWs128x128: {
             using TL = dm::Tile<128, 128>;
-            return launch<TL>(ws::kernel<TL>, A, B, C, M, N, K, stream, TL::T + 64);
+            return launch<TL>(ws::kernel<TL>, TL::T + 64, 1, A, B, C, M, N, K, stream);
         }
         case kGemmRs256x256: {
             using TL = rs::Tile<256, 256>;
-            return launch<TL>(rs::kernel<TL, 1>, A, B, C, M, N, K, stream);
+            return launch<TL>(rs::kernel<TL, 1>, TL::T, 1, A, B, C, M, N, K, stream);
         }
         case kGemmRs128x128: {
             using TL = rs::Tile<128, 128>;
-            return launch<TL>(rs::kernel<TL, 2>, A, B, C, M, N, K, stream);
+            return launch<TL>(rs::kernel<TL, 2>, TL::T, 1, A, B, C, M, N, K, stream);
         }
         default:
             return hipErrorInvalidValue;

@@ -32,6 +32,15 @@ struct TunedShape {
 hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N,
                            int64_t K, int variant, hipStream_t stream);
 
+// Split-K: `splits` workgroups per output tile, split s multiplying the K
+// range [s*chunk, min(K, (s+1)*chunk)) into the fp32 partial W + s*M*N, then
+// C = fp16(W_0 + W_1 + ... ) summed in ascending s (launch_splitk_sum).
+hipError_t launch_gemm_f16_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                                  int64_t K, int64_t chunk, int splits, float* W,
+                                  hipStream_t stream);
+hipError_t launch_splitk_sum(const float* W, _Float16* C, int64_t S, int64_t n,
+                             hipStream_t stream);
+
 // Elements per workgroup block of the streaming kernels (the block-size knob
 // of the pipelined elementwise add), chosen by measurement on MI355X: small
 // one-shot blocks keep many workgroups, and so many 16-byte loads, in flight.

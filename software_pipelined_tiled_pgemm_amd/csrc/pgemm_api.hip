@@ -50,6 +50,21 @@ int check_gemm(const void* A, const void* B, const void* C, int64_t M, int64_t N
     return PGEMM_OK;
 }
 
+constexpr int kMaxSplits = 64;
+constexpr int64_t kMaxSplitElems = (int64_t)1 << 36;  // M*N limit of the split-K path
+
+// K chunk of each split: ceil(K / splits) rounded up to a multiple of 64 (a
+// two-step period of the pipeline); the number of non-empty chunks.
+int64_t splitk_chunk(int64_t K, int splits) {
+    const int64_t c = (K + splits - 1) / splits;
+    return (c + 63) / 64 * 64;
+}
+int64_t splitk_parts(int64_t K, int splits) {
+    if (K <= 0) return 0;
+    const int64_t c = splitk_chunk(K, splits);
+    return (K + c - 1) / c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -70,6 +85,51 @@ int pgemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64
 }
 
 int pgemm_f16_num_variants(void) { return pgemm::kGemmNumVariants; }
+
+int pgemm_f16_splitk_default_splits(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return PGEMM_EINVAL;
+    // Enough (256x256 tile, chunk) pairs for the 256 CUs, chunks of at least
+    // 4096 (shorter chunks lose more to the partial traffic than they gain).
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    if (tiles == 0 || tiles >= 256) return 1;
+    int64_t s = (256 + tiles - 1) / tiles;
+    const int64_t by_k = K / 4096;
+    if (s > by_k) s = by_k;
+    if (s > 8) s = 8;
+    return s < 1 ? 1 : (int)s;
+}
+
+int64_t pgemm_f16_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splits) {
+    if (M < 0 || N < 0 || K < 0) return PGEMM_EINVAL;
+    if (splits < 1 || splits > kMaxSplits) return PGEMM_EUNSUPPORTED;
+    const int64_t parts = splitk_parts(K, splits);
+    if (parts <= 1 || M == 0 || N == 0) return 0;
+    if (N >= kMaxN || M >= kMaxM || M * N > kMaxSplitElems) return PGEMM_EUNSUPPORTED;
+    return parts * M * N * 4;
+}
+
+int pgemm_f16_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                     int splits, void* workspace, int64_t workspace_bytes,
+                     pgemm_stream_t stream) {
+    if (splits < 1 || splits > kMaxSplits) return PGEMM_EUNSUPPORTED;
+    const int rc = check_gemm(A, B, C, M, N, K);
+    if (rc != PGEMM_OK) return rc;
+    if (M == 0 || N == 0) return PGEMM_OK;
+    const int64_t parts = splitk_parts(K, splits);
+    if (parts <= 1)  // one chunk: exactly pgemm_f16
+        return hip_status(pgemm::launch_gemm_f16(A, B, C, M, N, K, pgemm::kGemmAuto,
+                                                 static_cast<hipStream_t>(stream)));
+    if (M * N > kMaxSplitElems) return PGEMM_EUNSUPPORTED;
+    const int64_t need = parts * M * N * 4;
+    if (!workspace || workspace_bytes < need) return PGEMM_EINVAL;
+    if (!aligned16(workspace)) return PGEMM_EUNSUPPORTED;
+    if (overlap(workspace, need, A, M * K * 2) || overlap(workspace, need, B, K * N * 2) ||
+        overlap(workspace, need, C, M * N * 2))
+        return PGEMM_EINVAL;
+    return hip_status(pgemm::launch_gemm_f16_splitk(
+        A, B, C, M, N, K, splitk_chunk(K, splits), (int)parts, static_cast<float*>(workspace),
+        static_cast<hipStream_t>(stream)));
+}
 
 int pgemm_f16_choose_variant(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return PGEMM_EINVAL;

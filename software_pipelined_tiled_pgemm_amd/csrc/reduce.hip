@@ -79,7 +79,50 @@ __global__ __launch_bounds__(kThreads) void sum_axis0_scalar_kernel(const float*
     o[j] = acc;
 }
 
+// Split-K finish: C[i] = fp16_rne(W[0][i] + W[1][i] + ... + W[S-1][i]), the
+// partials added in ascending order from +0.0f in fp32.  Lane t owns 8
+// consecutive outputs (two float4 per partial, one 16-byte fp16 store); n is
+// a multiple of 8 and both arrays are 16-byte aligned.
+__global__ __launch_bounds__(kThreads) void splitk_sum_kernel(const float* W, _Float16* C,
+                                                              int64_t S, int64_t n) {
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    typedef float float2_t __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // group of 8
+    if (8 * j >= n) return;
+    const floatx4* src = reinterpret_cast<const floatx4*>(W) + 2 * j;
+    const int64_t stride = n / 4;  // one partial, in float4
+    floatx4 lo = {0.0f, 0.0f, 0.0f, 0.0f}, hi = lo;
+    struct Part {
+        floatx4 a, b;
+    };
+    ring_pipeline<kRing, Part>(
+        S,
+        [&](int64_t s, Part& p) {
+            p.a = __builtin_nontemporal_load(src + s * stride);
+            p.b = __builtin_nontemporal_load(src + s * stride + 1);
+        },
+        [&](int64_t, const Part& p) {
+            lo += p.a;
+            hi += p.b;
+        });
+    u32x4 out;
+    out[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t{lo[0], lo[1]}), half2_t));
+    out[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t{lo[2], lo[3]}), half2_t));
+    out[2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t{hi[0], hi[1]}), half2_t));
+    out[3] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t{hi[2], hi[3]}), half2_t));
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(C) + j);
+}
+
 }  // namespace
+
+hipError_t launch_splitk_sum(const float* W, _Float16* C, int64_t S, int64_t n,
+                             hipStream_t stream) {
+    const int64_t groups = n / 8;
+    hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)((groups + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, W, C, S, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_sum_axis0(const float* x, float* o, int64_t R, int64_t n, hipStream_t stream) {
     const bool vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(o)) & 15u) == 0 &&

@@ -22,7 +22,8 @@ def L():
 
 def test_header_declares_the_boundary():
     names = _lib.declared_functions()
-    for n in ["pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants", "pstream_add",
+    for n in ["pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants", "pgemm_f16_splitk",
+              "pgemm_f16_splitk_workspace_bytes", "pgemm_f16_choose_variant", "pstream_add",
               "pstream_add_blocked", "pstream_add_scalar", "pgemm_test_fill_f32",
               "pgemm_test_iota_f32", "preduce_sum_f32", "pgemm_status_string", "pgemm_last_hip_error",
               "pgemm_version"]:
@@ -68,6 +69,44 @@ A, B, C = 0x10000000, 0x20000000, 0x30000000
 ])
 def test_gemm_argument_checks(L, args, expected):
     assert L.pgemm_f16(*args, None) == expected
+
+
+def test_splitk_workspace_bytes(L):
+    wb = L.pgemm_f16_splitk_workspace_bytes
+    assert wb(2048, 2048, 32768, 4) == 4 * 2048 * 2048 * 4
+    assert wb(64, 64, 64, 4) == 0                  # one 64-element chunk
+    assert wb(64, 64, 200, 4) == 4 * 64 * 64 * 4   # chunks of 64: 64, 64, 64, 8
+    assert wb(64, 64, 136, 2) == 2 * 64 * 64 * 4   # chunks of 128: 128, 8
+    assert wb(64, 64, 1000, 3) == 3 * 64 * 64 * 4  # chunks of 384
+    assert wb(0, 64, 1000, 3) == 0 and wb(64, 64, 0, 3) == 0
+    assert wb(-1, 8, 8, 2) == EINVAL
+    assert wb(8, 8, 8, 0) == EUNSUP and wb(8, 8, 8, 65) == EUNSUP
+
+
+@pytest.mark.parametrize("args,expected", [
+    ((A, B, C, 64, 64, 512, 4, 0, 1 << 20), EINVAL),              # no workspace
+    ((A, B, C, 64, 64, 512, 4, 0x40000000, 1000), EINVAL),        # too small
+    ((A, B, C, 64, 64, 512, 4, 0x40000008, 1 << 20), EUNSUP),     # misaligned
+    ((A, B, C, 64, 64, 512, 4, A, 1 << 20), EINVAL),              # overlaps A
+    ((A, B, C, 64, 64, 512, 0, 0x40000000, 1 << 20), EUNSUP),     # splits out of range
+    ((A, B, C, 64, 64, 512, 65, 0x40000000, 1 << 20), EUNSUP),
+    ((A, B, C, 64, 12, 512, 4, 0x40000000, 1 << 20), EUNSUP),     # N % 8
+    ((A, B, C, -1, 64, 512, 4, 0x40000000, 1 << 20), EINVAL),
+    ((0, 0, 0, 0, 64, 512, 4, 0, 0), OK),                         # empty: nothing enqueued
+])
+def test_splitk_argument_checks(L, args, expected):
+    assert L.pgemm_f16_splitk(*args, None) == expected
+
+
+def test_splitk_default_splits(L):
+    d = L.pgemm_f16_splitk_default_splits
+    assert d(2048, 2048, 32768) == 4      # 64 tiles, chunks of 8192
+    assert d(1024, 1024, 16384) == 4      # 16 tiles would want 16; chunks >= 4096
+    assert d(2048, 2048, 2048) == 1       # short K
+    assert d(4096, 4096, 16384) == 1      # 256 tiles already
+    assert d(256, 256, 1 << 21) == 8      # capped at 8
+    assert d(0, 8, 8) == 1
+    assert d(-1, 8, 8) == EINVAL
 
 
 def test_gemm_variant_range(L):

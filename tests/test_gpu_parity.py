@@ -352,6 +352,87 @@ def test_gemm_full_size_sampled(name, M, N, K, dist):
     say("  sample %d points: max |ulp diff| %d, frac exact %.4f" % (I.size, d.max(), np.mean(d == 0)))
 
 
+# ------------------------------------------------------------ split-K GEMM
+
+def splitk(A, B, splits):
+    say("  gemm split-K M=%d N=%d K=%d splits=%d" % (A.shape[0], B.shape[1], A.shape[1], splits))
+    tA = A if isinstance(A, torch.Tensor) else dev(A)
+    tB = B if isinstance(B, torch.Tensor) else dev(B)
+    return host(pg.pgemm_f16_splitk(tA, tB, splits))
+
+
+# (M, N, K, splits): several tiles, ragged edges, K not a multiple of the
+# 64-element chunk granule, more splits than chunks, an odd number of steps
+# per chunk, and both tile sizes of the split path (few and many tiles).
+SPLITK_CASES = [(64, 64, 512, 2), (200, 136, 1000, 3), (256, 256, 4096, 4), (300, 264, 2056, 7),
+                (520, 776, 136, 2), (128, 128, 64, 4), (96, 520, 1088, 5), (1024, 1024, 2048, 2)]
+
+
+@pytest.mark.parametrize("M,N,K,splits", SPLITK_CASES)
+def test_gemm_splitk_vs_full_oracle(M, N, K, splits):
+    A, B = inputs.gemm_inputs(M, N, K)
+    ref, _ = oracle.gemm_f16(A, B)
+    got = splitk(A, B, splits)
+    assert_close(got, ref, "split-K %dx%dx%d/%d" % (M, N, K, splits))
+    assert bits_equal(got, splitk(A, B, splits)), "split-K is not deterministic"
+
+
+def test_gemm_splitk_one_chunk_is_pgemm():
+    A, B = inputs.gemm_inputs(256, 264, 64)
+    assert pg.pgemm_f16_splitk_workspace_bytes(256, 264, 64, 4) == 0
+    assert bits_equal(splitk(A, B, 4), gemm(A, B))
+    A, B = inputs.gemm_inputs(128, 128, 1024)
+    assert bits_equal(splitk(A, B, 1), gemm(A, B))
+
+
+def test_gemm_splitk_identity_and_ones_exact():
+    # identity: each output has one non-zero product, in one chunk -> exact,
+    # subnormals included (no -0: sums start from +0, so -0 comes out +0 on
+    # every path, the oracle's included)
+    rng = np.random.default_rng(9)
+    Bm = _finite_f16_no_negzero(rng, (512, 264))
+    I = np.eye(512, dtype=np.float16)
+    ref, _ = oracle.gemm_f16(I, Bm)
+    assert bits_equal(ref, Bm)
+    got = splitk(I, Bm, 4)
+    assert bits_equal(got, ref), "split-K identity: first mismatches %s" % np.argwhere(
+        got.view(np.uint16) != ref.view(np.uint16))[:8]
+    # ones: every partial is an integer below 2^24 -> C = K exactly
+    M, N, K = 2048, 2048, 32768
+    ones = torch.ones((M, K), dtype=torch.float16, device="cuda:0")
+    onesb = torch.ones((K, N), dtype=torch.float16, device="cuda:0")
+    got = host(pg.pgemm_f16_splitk(ones, onesb, 4))
+    assert np.all(got == np.float16(K))
+
+
+def test_gemm_splitk_full_size_sampled():
+    M, N, K = 2048, 2048, 32768
+    say("gemm split-K full size %dx%dx%d" % (M, N, K))
+    A, B = inputs.gemm_inputs(M, N, K)
+    got = splitk(A, B, 4)
+    I, J = inputs.sample_points(M, N, 8192)
+    ref, _ = oracle.gemm_f16_points(A, B, I, J)
+    assert_close(got[I, J], ref, "split-K long K")
+
+
+def test_gemm_splitk_device_argument_checks():
+    L = pg.lib()
+    buf = torch.zeros(1 << 20, dtype=torch.float16, device="cuda:0")
+    p = buf.data_ptr()
+    A, B, C, W = p, p + (1 << 18), p + (2 << 18), p + (3 << 18)
+    M = N = 64
+    K = 512
+    need = L.pgemm_f16_splitk_workspace_bytes(M, N, K, 4)
+    assert need == 4 * M * N * 4
+    s = None
+    assert L.pgemm_f16_splitk(A, B, C, M, N, K, 4, 0, need, s) == pg.PGEMM_EINVAL
+    assert L.pgemm_f16_splitk(A, B, C, M, N, K, 4, W, need - 16, s) == pg.PGEMM_EINVAL
+    assert L.pgemm_f16_splitk(A, B, C, M, N, K, 4, W + 8, need, s) == pg.PGEMM_EUNSUPPORTED
+    assert L.pgemm_f16_splitk(A, B, C, M, N, K, 4, C, need, s) == pg.PGEMM_EINVAL  # overlaps C
+    assert L.pgemm_f16_splitk(A, B, C, M, N, K, 0, W, need, s) == pg.PGEMM_EUNSUPPORTED
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------ reduction (guide 7.2)
 
 def test_sum_axis0_pages_worked_example():
