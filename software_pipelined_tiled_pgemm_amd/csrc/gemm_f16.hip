@@ -88,7 +88,13 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, int64_t bytes) {
 // offset past the buffer size writes zeros.  Written as inline assembly so
 // the compiler does not treat later LDS reads as possibly aliasing it and
 // wait for every copy in flight: the pipeline orders copies and reads itself,
-// with explicit vmcnt waits and workgroup barriers.
+// with explicit vmcnt waits and workgroup barriers.  M0 is clobbered and
+// reloaded by every copy; the compiler warns that it will not preserve M0
+// across the statement, which is harmless here because no other code in
+// these kernels uses M0 (every M0 access in the generated assembly is one of
+// these copies' own s_mov).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t off, uint32_t lds) {
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
@@ -98,6 +104,7 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t off, uint32_t lds) {
         : "v"(off), "s"(rsrc), "s"(lds)
         : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const LDS_AS char*)p;

@@ -475,3 +475,15 @@ def test_sum_axis0_misaligned_view_scalar_path():
     tx = dev(flat)[1:].view(R, n)
     got = host(pg.preduce_sum_f32(tx))
     assert bits_equal(got, oracle.sum_axis0_f32(flat[1:].reshape(R, n)))
+
+
+# ------------------------------------------------------------ autotuner on the device
+
+def test_autotune_measures_every_variant():
+    from software_pipelined_tiled_pgemm_amd import autotune
+    say("autotune: 256^3, variants 1 and 2, one round")
+    recs = autotune.measure([(256, 256, 256)], variants=[1, 2], rounds=1, target_s=0.002)
+    assert len(recs) == 1 and set(recs[0]["tflops"]) == {1, 2}
+    assert all(x > 0 for x in recs[0]["tflops"].values())
+    table = autotune.parse_table(autotune.render_table(recs, "test"))
+    assert table == [(256, 256, 256, autotune.fastest(recs[0]))]
