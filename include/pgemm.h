@@ -86,9 +86,14 @@ int pgemm_f16(const void* A, const void* B, void* C,
  *   6  128x128 output tile, wave-specialised: 4 waves only read LDS and
  *      multiply, a fifth wave issues every global->LDS copy and waits for
  *      them (the pages' warp-specialised pipeline); ring and copy order as 2
- * Every variant gives bit-identical results for the same inputs (the K
- * order inside each output element depends neither on the tiling nor on
- * the pipeline).
+ *   7  as 2, on the 16x16x32 matrix instruction (one instruction per 16x16
+ *      output block and K step of 32 instead of two 32x32x16 ones)
+ *   8  as 5, on the 16x16x32 instruction
+ * Variants 1-6 give bit-identical results for the same inputs, and so do
+ * variants 7-8: inside a family the grouping of the K sum of each output
+ * element depends neither on the tiling nor on the pipeline.  The two
+ * families group the products differently (16 vs 32 per instruction), so
+ * they may differ in the last bits; both are within the accuracy bound.
  * Unknown variants return PGEMM_EUNSUPPORTED.
  */
 int pgemm_f16_variant(const void* A, const void* B, void* C,

@@ -4,6 +4,8 @@
 
 Flags: -O3; packed-fp32 instructions disabled; fp32 denormals kept (the
 streaming kernels must match IEEE binary32 bit for bit); no fast-math.
+Each source is compiled to an object (PER_FILE adds flags to single
+sources), then the objects are linked into the shared library.
 """
 from __future__ import annotations
 
@@ -19,12 +21,13 @@ LIB = os.path.join(PKG, "libpgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
+OBJDIR = os.path.join(PKG, "_build")
+
 FLAGS = [
     "--offload-arch=" + ARCH,
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-fno-gpu-flush-denormals-to-zero",
     "-fno-fast-math",
     "-ffp-contract=off",
@@ -33,15 +36,20 @@ FLAGS = [
     "-Wall",
 ]
 
+# Extra code-generation flags of single sources.
+PER_FILE = {
+    # The 16x16x32 GEMM kernels: MFMA results in ordinary VGPRs (without it
+    # the compiler moves accumulator blocks between register files inside
+    # the K loop; see the file's header comment).
+    "gemm_f16_m16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every HIP source into libpgemm.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + list(extra_flags or []) + sources() + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,6 +59,28 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, out))
     if verbose and out.strip():
         print(out)
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every HIP source and link libpgemm.so (always recompiles)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(OBJDIR, exist_ok=True)
+    tag = ".%d" % os.getpid()
+    jobs = []
+    for src in sources():
+        name = os.path.basename(src)
+        obj = os.path.join(OBJDIR, name + tag + ".o")
+        cmd = ([HIPCC] + FLAGS + PER_FILE.get(name, []) + list(extra_flags or [])
+               + ["-c", src, "-o", obj])
+        jobs.append((cmd, obj))
+    with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    objs = [o for _, o in jobs]
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
+    for o in objs:
+        os.remove(o)
     os.replace(tmp, LIB)
     return LIB
 

@@ -16,7 +16,12 @@ enum GemmVariant : int {
     kGemmRs128x128 = 4,  // register-staged pipeline, 2 LDS stages of K 64
     kGemm256x256w8 = 5,  // LDS-DMA pipeline, 8 waves (2 per SIMD), 128x64 per wave
     kGemmWs128x128 = 6,  // wave-specialised LDS-DMA pipeline: 4 MFMA waves + 1 copy wave
-    kGemmNumVariants = 6,
+    // The same LDS-DMA pipeline on v_mfma_f32_16x16x32_f16 (one MFMA per
+    // 16x16 block and K step of 32).  A different accumulation grouping, so
+    // results are bit-identical within this family, not with variants 1-6.
+    kGemm128x128m16 = 7,    // 4 waves, 64x64 per wave, 2 workgroups per CU
+    kGemm256x256w8m16 = 8,  // 8 waves (2 per SIMD), 128x64 per wave
+    kGemmNumVariants = 8,
 };
 
 // Picks a concrete variant for a problem shape: the variant measured fastest
@@ -31,6 +36,9 @@ struct TunedShape {
 
 hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N,
                            int64_t K, int variant, hipStream_t stream);
+// Variants of the 16x16x32 family (gemm_f16_m16.hip).
+hipError_t launch_gemm_f16_m16(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                               int64_t K, int variant, hipStream_t stream);
 
 // Split-K: `splits` workgroups per output tile, split s multiplying the K
 // range [s*chunk, min(K, (s+1)*chunk)) into the fp32 partial W + s*M*N, then
