@@ -16,7 +16,7 @@
 //  * copy_start early / copy_wait late with several buffers (Pallas
 //    software-pipelining guide, section 4; max_concurrent_steps of the
 //    quickstart's emit_pipeline).  Two pipelines are implemented:
-//      - LDS-DMA pipeline (variants 1, 2, 5): a ring of 5 LDS stages of
+//      - LDS-DMA pipeline (variants 1, 2, 5, 7, 8): a ring of 5 LDS stages of
 //        BK = 32.  copy_start is a buffer_load ... lds (global memory
 //        straight into LDS, no registers), issued 2 to 4 steps ahead and
 //        spread over the MFMA slots; copy_wait is an s_waitcnt on this
@@ -28,19 +28,21 @@
 //    stage is refilled only after every wave has passed the barrier that
 //    follows its last ds_read of it.  MFMA operands are VGPRs, so no matrix
 //    instruction can still be reading LDS at that point.
-//  * fp32 accumulator in registers (the quickstart's ACC): 32x32 MFMA blocks
-//    held in VGPR/AGPR for the whole K loop, zeroed before step 0 (the
-//    initialise-before-accumulate rule of the guide, section 7.2).
+//  * fp32 accumulator in registers (the quickstart's ACC): 32x32 or 16x16
+//    MFMA blocks held in VGPR/AGPR for the whole K loop, zeroed before step 0
+//    (the initialise-before-accumulate rule of the guide, section 7.2).
 //  * Drain (quickstart's epilogue: cast, stage through shared memory, copy
 //    out): fp32 -> fp16, written to LDS, then 16-byte coalesced row stores.
 //
-// Matrix instruction: v_mfma_f32_32x32x16_f16 (32x32 output block, 16-deep
-// K, 8 fp16 per lane per operand; lanes 0-31 carry K 0..7, lanes 32-63 K
-// 8..15).  Each MFMA computes the transposed block C^T = B^T A^T (B^T as the
-// row operand), so that each lane ends up holding four consecutive columns of
-// one row of C -- 8 contiguous bytes for the epilogue.  Every variant feeds
-// the MFMAs the same K blocks in the same order, so all variants produce
-// bit-identical results.
+// Matrix instructions: v_mfma_f32_32x32x16_f16 (variants 1-6: 32x32 output
+// block, 16-deep K, 8 fp16 per lane per operand; lanes 0-31 carry K 0..7,
+// lanes 32-63 K 8..15) and v_mfma_f32_16x16x32_f16 (variants 7, 8: 16x16
+// block, the whole K 32 of a stage; see Compute<TL, 16>).  Each MFMA computes
+// the transposed block C^T = B^T A^T (B^T as the row operand), so that each
+// lane ends up holding four consecutive columns of one row of C -- 8
+// contiguous bytes for the epilogue.  Within one instruction family every
+// variant feeds the MFMAs the same K blocks in the same order, so its
+// variants produce bit-identical results.
 //
 // Edge tiles: buffer loads return zero outside the matrix (rows >= M,
 // K >= K, columns >= N); stores are masked.
