@@ -832,7 +832,6 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
         // second step multiplies the zeros its copies read past the end of
         // K, which leaves every accumulator unchanged (they start at +0 and
         // never become -0, so adding +0 is exact).
-        int se = 0;  // slot of step kt
         // Periods whose copies (steps kt+4, kt+5) lie inside K take the
         // steady-state copies; the last ones, and all of a short K, the
         // general ones.  Same data either way.
@@ -840,8 +839,11 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
         const int64_t bstep = (int64_t)BK * N;          // elements per B step
         const _Float16* b4 = B + n0 + 4 * bstep;         // rows of step kt+4
         uint32_t a4 = 4 * BK * 2;                        // A byte offset of step kt+4
-        auto period = [&](int kt, auto fast) __attribute__((always_inline)) {
+        // One period; `slot` is the ring slot of step kt, either the run-time
+        // `se` or a compile-time constant (the unrolled loop below).
+        auto period = [&](int kt, auto fast, auto slot) __attribute__((always_inline)) {
             constexpr bool F = decltype(fast)::value;
+            const int se = slot;
             const int s1 = wrap5(se + 1), s2 = wrap5(se + 2), s4 = wrap5(se + 4);
             const char* cur = smem + se * TL::STAGE;
             const char* nxt = smem + s1 * TL::STAGE;
@@ -882,14 +884,26 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
                                        else
                                            cp.issue_b(q, B, N, K, n0, (kt + 5) * BK, st5, wave);
                                    });
-            se = s2;
             b4 += 2 * bstep;
             a4 += 2 * BK * 2;
+            return s2;
         };
+        using std::integral_constant;
         const int fast_end = K / BK - 5;  // kt < fast_end <=> step kt+5 is a full step
         int kt = 0;
-        for (; kt < fast_end && kt < nk; kt += 2) period(kt, std::true_type{});
-        for (; kt < nk; kt += 2) period(kt, std::false_type{});
+        // Five periods (ten steps) bring the ring back to slot 0, so the
+        // unrolled loop knows every slot at compile time: no slot arithmetic
+        // between the MFMAs.
+        for (; kt + 8 < fast_end && kt + 8 < nk; kt += 10) {
+            period(kt, std::true_type{}, integral_constant<int, 0>{});
+            period(kt + 2, std::true_type{}, integral_constant<int, 2>{});
+            period(kt + 4, std::true_type{}, integral_constant<int, 4>{});
+            period(kt + 6, std::true_type{}, integral_constant<int, 1>{});
+            period(kt + 8, std::true_type{}, integral_constant<int, 3>{});
+        }
+        int se = 0;  // slot of step kt
+        for (; kt < fast_end && kt < nk; kt += 2) se = period(kt, std::true_type{}, se);
+        for (; kt < nk; kt += 2) se = period(kt, std::false_type{}, se);
         wait_vmcnt<0>();  // drain the copies of the steps past the end
     }
     __syncthreads();  // every wave is done with the stage ring
