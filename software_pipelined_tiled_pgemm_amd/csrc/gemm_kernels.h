@@ -901,16 +901,30 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
             period(kt + 6, std::true_type{}, integral_constant<int, 1>{});
             period(kt + 8, std::true_type{}, integral_constant<int, 3>{});
         }
+        // The tail periods recompute the per-lane copy offsets instead of
+        // keeping them live across the unrolled loop (same values; the empty
+        // statement hides that from the compiler).
+        {
+            int l = lane;
+            asm volatile("" : "+v"(l));
+            cp.init(l, wave, Kfull, N, n0);
+        }
         int se = 0;  // slot of step kt
         for (; kt < fast_end && kt < nk; kt += 2) se = period(kt, std::true_type{}, se);
         for (; kt < nk; kt += 2) se = period(kt, std::false_type{}, se);
         wait_vmcnt<0>();  // drain the copies of the steps past the end
     }
     __syncthreads();  // every wave is done with the stage ring
+    // The drain derives its lane addresses from the thread index afresh (the
+    // empty statement hides that it is the same value), so that no values
+    // derived before the K loop stay live across it: the loop runs at the
+    // register limit.
+    int tid_d = tid;
+    asm volatile("" : "+v"(tid_d));
     if constexpr (SPLIT)
-        cm.drain_w(smem, W + (int64_t)blockIdx.y * M * N, M, N, m0, n0, tid, wm, wn);
+        cm.drain_w(smem, W + (int64_t)blockIdx.y * M * N, M, N, m0, n0, tid_d, wm, wn);
     else
-        cm.drain_c(smem, C, M, N, m0, n0, tid, wm, wn);
+        cm.drain_c(smem, C, M, N, m0, n0, tid_d, wm, wn);
 }
 
 }  // namespace dm
