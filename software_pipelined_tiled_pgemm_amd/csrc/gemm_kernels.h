@@ -813,16 +813,37 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
             const int t = t0 + (q >> 1), h = q & 1;
             cp.issue_a(t, A, M, K, m0, (s + h) * BK, ring + (h ? sb : sa) * TL::STAGE, wave);
         };
-        // Prologue: steps 0..3, in the order a period issues them.
+        // Prologue: steps 0..3, in the order a period issues them; with the
+        // steady-state copies when all four steps lie inside K.
+        cp.init_fast(A, M, m0, N, n0);
+        const int64_t bstep = (int64_t)BK * N;  // elements per B step
+        if (K >= 4 * BK) {
 #pragma unroll
-        for (int e = 0; e < 4; e += 2) {
+            for (int e = 0; e < 4; e += 2) {
+                const uint32_t ste = ring + e * TL::STAGE;
 #pragma unroll
-            for (int t = 0; t < H; ++t) cp.issue_b(t, B, N, K, n0, e * BK, ring + e * TL::STAGE, wave);
+                for (int t = 0; t < H; ++t) cp.fast_b(t, B + n0 + e * bstep, ste, wave);
 #pragma unroll
-            for (int q = 0; q < 2 * H; ++q) a_pairs(q, 0, e, e, e + 1);
+                for (int q = 0; q < 2 * H; ++q) {
+                    const int h = q & 1;
+                    cp.fast_a(q >> 1, (uint32_t)((e + h) * BK * 2), ste + h * TL::STAGE, wave);
+                }
 #pragma unroll
-            for (int t = 0; t < H; ++t)
-                cp.issue_b(t, B, N, K, n0, (e + 1) * BK, ring + (e + 1) * TL::STAGE, wave);
+                for (int t = 0; t < H; ++t)
+                    cp.fast_b(t, B + n0 + (e + 1) * bstep, ste + TL::STAGE, wave);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+#pragma unroll
+                for (int t = 0; t < H; ++t)
+                    cp.issue_b(t, B, N, K, n0, e * BK, ring + e * TL::STAGE, wave);
+#pragma unroll
+                for (int q = 0; q < 2 * H; ++q) a_pairs(q, 0, e, e, e + 1);
+#pragma unroll
+                for (int t = 0; t < H; ++t)
+                    cp.issue_b(t, B, N, K, n0, (e + 1) * BK, ring + (e + 1) * TL::STAGE, wave);
+            }
         }
         wait_vmcnt<5 * H>();  // this wave's copies of step 0 landed ...
         __syncthreads();      // ... and every other wave's
@@ -835,8 +856,6 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
         // Periods whose copies (steps kt+4, kt+5) lie inside K take the
         // steady-state copies; the last ones, and all of a short K, the
         // general ones.  Same data either way.
-        cp.init_fast(A, M, m0, N, n0);
-        const int64_t bstep = (int64_t)BK * N;          // elements per B step
         const _Float16* b4 = B + n0 + 4 * bstep;         // rows of step kt+4
         uint32_t a4 = 4 * BK * 2;                        // A byte offset of step kt+4
         // One period; `slot` is the ring slot of step kt, either the run-time
