@@ -202,6 +202,12 @@ SMALL_SHAPES = [
     (255, 248, 1000),
     (520, 776, 136),
     (64, 1024, 8),
+    # K-loop structure boundaries (steps of 32; steady-state periods unrolled
+    # by five, then run-time steady-state periods, then tail periods):
+    (136, 264, 448),   # 14 steps: one unrolled pass, then tail periods
+    (264, 136, 416),   # 13 steps: no unrolled pass, odd step count
+    (256, 256, 480),   # 15 steps
+    (128, 384, 832),   # 26 steps: two unrolled passes, a run-time one, tail
 ]
 
 
