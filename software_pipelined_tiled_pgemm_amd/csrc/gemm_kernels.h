@@ -219,7 +219,9 @@ __device__ __forceinline__ void drain(char* smem, floatx16 (&acc)[FN][FM], _Floa
 
 // Second half of a drain: the fp16 tile in LDS (16-byte chunk c of row r at
 // c ^ (r mod chunks-per-row)) to C with 16-byte row stores.
-// Thread t stores chunk t % CH of rows t / CH + (T / CH) * r.
+// Thread t stores chunk t % CH of rows t / CH + (T / CH) * r.  The stores are
+// non-temporal: this kernel never reads C, and streaming it out keeps the
+// caches for the operand tiles that other workgroups still fetch.
 template <int BM, int BN, int T>
 __device__ __forceinline__ void store_tile(const char* smem, _Float16* C, int M, int N, int m0,
                                            int n0, int tid) {
@@ -237,7 +239,7 @@ __device__ __forceinline__ void store_tile(const char* smem, _Float16* C, int M,
             const int pchunk = chunk ^ (row & (CH - 1));
             const u32x4 v =
                 *reinterpret_cast<const u32x4*>(src + r * RSTEP * (BN * 2) + pchunk * 16);
-            *reinterpret_cast<u32x4*>(dst + r * dstep) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + r * dstep));
         }
     } else {
         const bool col_ok = n0 + chunk * 8 < N;
@@ -247,7 +249,8 @@ __device__ __forceinline__ void store_tile(const char* smem, _Float16* C, int M,
             const int pchunk = chunk ^ (row & (CH - 1));
             const u32x4 v =
                 *reinterpret_cast<const u32x4*>(src + r * RSTEP * (BN * 2) + pchunk * 16);
-            if (col_ok && m0 + row < M) *reinterpret_cast<u32x4*>(dst + r * dstep) = v;
+            if (col_ok && m0 + row < M)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + r * dstep));
         }
     }
 }

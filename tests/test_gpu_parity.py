@@ -362,6 +362,37 @@ def test_gemm_full_size_sampled(name, M, N, K, dist):
     say("  sample %d points: max |ulp diff| %d, frac exact %.4f" % (I.size, d.max(), np.mean(d == 0)))
 
 
+# ------------------------------------------------------------ one GPU's row shard
+
+# Split G ways by rows of C, GPU g computes A's row block g times all of B
+# (output tiles are independent).  One GPU's share of each product below is
+# its (M/8) x N x K block: checked against the oracle with the variant chosen
+# for the shard shape, and, run with the variant of the whole product,
+# bit-identical to the same rows of the whole product.
+SHARD_CASES = [(4096, 4096, 4096, "uniform"), (2048, 2048, 32768, "uniform")]
+
+
+@pytest.mark.parametrize("M,N,K,dist", SHARD_CASES, ids=["%dx%dx%d" % c[:3] for c in SHARD_CASES])
+def test_gemm_row_shards(M, N, K, dist):
+    G = 8
+    L = pg.lib()
+    A, B = inputs.gemm_inputs(M, N, K, dist)
+    tA, tB = dev(A), dev(B)
+    v_full = L.pgemm_f16_choose_variant(M, N, K)
+    full = gemm(tA, tB, v_full)
+    m = M // G
+    say("gemm %d-way row shards of %dx%dx%d: shard variant %d, whole-product variant %d"
+        % (G, M, N, K, L.pgemm_f16_choose_variant(m, N, K), v_full))
+    for g in (0, 3, G - 1):
+        rows = slice(g * m, (g + 1) * m)
+        shard = gemm(tA[rows], tB)  # automatic variant at the shard shape
+        I, J = inputs.sample_points(m, N, 2048, seed=10 + g, full_rows=8, full_cols=8)
+        ref, _ = oracle.gemm_f16_points(A[rows], B, I, J)
+        assert_close(shard[I, J], ref, "shard %d of %dx%dx%d" % (g, M, N, K))
+        same = gemm(tA[rows], tB, v_full)
+        assert np.array_equal(same.view(np.uint16), full[rows].view(np.uint16)), "shard %d" % g
+
+
 # ------------------------------------------------------------ split-K GEMM
 
 def splitk(A, B, splits):
