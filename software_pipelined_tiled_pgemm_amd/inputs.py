@@ -11,6 +11,11 @@ conversion to the storage type):
   elementwise example of the Pallas software-pipelining guide, section 6.
 * GEMM, normal: N(0, std = 1/sqrt(K)), same seeds, stored as float16.
 * Streaming add: x = U[-1,1] seed 0, y = U[-1,1] seed 1, stored as float32.
+
+For operands too large to draw on the host (several GiB), ``hashed_f16``
+defines element (r, c) of a matrix by an integer hash of its indices, so any
+row or column subset can be rebuilt on the host and the whole matrix drawn
+on the device (``hashed_f16_torch``, the same integer steps in torch).
 """
 from __future__ import annotations
 
@@ -77,3 +82,42 @@ def sample_points(M: int, N: int, n_points: int, seed: int = 2,
     J = np.concatenate(J).astype(np.int64)
     key = np.unique(I * N + J)
     return (key // N).astype(np.int64), (key % N).astype(np.int64)
+
+
+def _hash_values(r, c, seed, xor, shr):
+    """Integer steps of ``hashed_f16`` (non-negative int64 throughout, no
+    overflow: r, c < 2**31)."""
+    m31 = 2147483647  # x & m31 == x mod 2**31 for x >= 0
+    h = xor((r * 2654435761) & m31, (c * 40503 + seed * 7919) & m31)
+    h = (xor(h, shr(h, 15)) * 2246822519) & m31
+    h = xor(h, shr(h, 13)) % 2039
+    return h - 1019
+
+
+def hashed_f16(rows, cols, seed: int) -> np.ndarray:
+    """Matrix [len(rows), len(cols)] with element (r, c) = (hash(r, c, seed)
+    - 1019) / 1024, hash in 0..2038: multiples of 2**-10 in [-1019/1024, 1019/1024],
+    all exact in float16."""
+    r = np.asarray(rows, dtype=np.int64)[:, None]
+    c = np.asarray(cols, dtype=np.int64)[None, :]
+    out = np.empty((r.shape[0], c.shape[1]), dtype=np.float16)
+    step = max(1, (1 << 20) // max(1, c.shape[1]))  # rows per chunk: small temporaries
+    for r0 in range(0, r.shape[0], step):
+        v = _hash_values(r[r0:r0 + step], c, seed, np.bitwise_xor, np.right_shift)
+        out[r0:r0 + step] = (v.astype(np.float64) / 1024.0).astype(np.float16)
+    return out
+
+
+def hashed_f16_torch(n_rows: int, n_cols: int, seed: int, device, row_chunk: int = 2048):
+    """The [n_rows, n_cols] ``hashed_f16`` matrix (rows 0.., columns 0..) as a
+    float16 torch tensor on ``device``, built in row chunks of at most
+    ``row_chunk`` rows and 2**25 elements."""
+    import torch
+    row_chunk = max(1, min(row_chunk, (1 << 25) // max(1, n_cols)))
+    out = torch.empty((n_rows, n_cols), dtype=torch.float16, device=device)
+    c = torch.arange(n_cols, dtype=torch.int64, device=device)[None, :]
+    for r0 in range(0, n_rows, row_chunk):
+        r = torch.arange(r0, min(n_rows, r0 + row_chunk), dtype=torch.int64, device=device)[:, None]
+        v = _hash_values(r, c, seed, torch.bitwise_xor, torch.bitwise_right_shift)
+        out[r0:r0 + r.shape[0]] = (v.to(torch.float64) / 1024.0).to(torch.float16)
+    return out

@@ -393,6 +393,34 @@ def test_gemm_row_shards(M, N, K, dist):
         assert np.array_equal(same.view(np.uint16), full[rows].view(np.uint16)), "shard %d" % g
 
 
+# ------------------------------------------------------------ operands beyond 4 GiB
+
+# One operand of more than 4 GiB per case, so byte offsets into A, B or C pass
+# 32 bits (every variant).  Elements come from the index hash, so the oracle
+# rebuilds only the rows of A and columns of B that the sampled outputs need.
+BIG_CASES = [("A", 135000, 264, 16384), ("B", 136, 1048584, 2048), ("C", 65600, 32776, 64)]
+
+
+@pytest.mark.parametrize("which,M,N,K", BIG_CASES, ids=["%s over 4 GiB" % c[0] for c in BIG_CASES])
+def test_gemm_operand_beyond_4gib(which, M, N, K):
+    say("gemm with %s over 4 GiB: M=%d N=%d K=%d" % (which, M, N, K))
+    tA = inputs.hashed_f16_torch(M, K, inputs.SEED_A, "cuda:0")
+    tB = inputs.hashed_f16_torch(K, N, inputs.SEED_B, "cuda:0")
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+    assert {"A": tA, "B": tB, "C": C}[which].numel() * 2 > 1 << 32
+    I, J = inputs.sample_points(M, N, 2048, seed=3, full_rows=0, full_cols=0)
+    rows, Iu = np.unique(I, return_inverse=True)
+    cols, Ju = np.unique(J, return_inverse=True)
+    ref, _ = oracle.gemm_f16_points(inputs.hashed_f16(rows, np.arange(K), inputs.SEED_A),
+                                    inputs.hashed_f16(np.arange(K), cols, inputs.SEED_B), Iu, Ju)
+    tI, tJ = torch.from_numpy(I).to("cuda:0"), torch.from_numpy(J).to("cuda:0")
+    for v in [0] + VARIANTS:
+        say("  variant %d" % v)
+        C.fill_(float("nan"))
+        pg.pgemm_f16_variant(tA, tB, v, C=C)
+        assert_close(host(C[tI, tJ]), ref, "%s over 4 GiB, variant %d" % (which, v))
+
+
 # ------------------------------------------------------------ split-K GEMM
 
 def splitk(A, B, splits):
