@@ -399,6 +399,7 @@ def test_gemm_row_shards(M, N, K, dist):
 # 32 bits (every variant).  Elements come from the index hash, so the oracle
 # rebuilds only the rows of A and columns of B that the sampled outputs need.
 BIG_CASES = [("A", 135000, 264, 16384), ("B", 136, 1048584, 2048), ("C", 65600, 32776, 64)]
+BIG_SPLITS = {"A": 4, "B": 2, "C": None}  # split-K too where K has several chunks
 
 
 @pytest.mark.parametrize("which,M,N,K", BIG_CASES, ids=["%s over 4 GiB" % c[0] for c in BIG_CASES])
@@ -419,6 +420,11 @@ def test_gemm_operand_beyond_4gib(which, M, N, K):
         C.fill_(float("nan"))
         pg.pgemm_f16_variant(tA, tB, v, C=C)
         assert_close(host(C[tI, tJ]), ref, "%s over 4 GiB, variant %d" % (which, v))
+    if BIG_SPLITS[which]:
+        say("  split-K, %d splits" % BIG_SPLITS[which])
+        C.fill_(float("nan"))
+        pg.pgemm_f16_splitk(tA, tB, BIG_SPLITS[which], C=C)
+        assert_close(host(C[tI, tJ]), ref, "%s over 4 GiB, split-K" % which)
 
 
 # ------------------------------------------------------------ split-K GEMM
