@@ -189,6 +189,55 @@ def test_stream_add_scalar_ragged_and_specials(n):
         assert bits_equal(host(pg.pstream_add_scalar(dev(x), c)), oracle.add_scalar_f32(x, c))
 
 
+# Arrays of more than 4 GiB: element offsets past 2**30 floats.  x and y come
+# from the index hash (viewed as rows of 1029), y scaled by float32(0.3) so
+# that the sums round; the oracle rebuilds the sampled elements on the host.
+BIG_N_COLS, BIG_N_ROWS = 1029, 1043500  # n = 1 073 761 500 > 2**30
+
+
+def _big_vector(seed):
+    t = inputs.hashed_f16_torch(BIG_N_ROWS, BIG_N_COLS, seed, "cuda:0").view(-1).float()
+    return t if seed == inputs.SEED_A else t.mul_(np.float32(0.3))
+
+
+def _big_vector_at(idx, seed):
+    rows, inv = np.unique(idx // BIG_N_COLS, return_inverse=True)
+    v = inputs.hashed_f16(rows, np.arange(BIG_N_COLS), seed)[inv, idx % BIG_N_COLS].astype(np.float32)
+    return v if seed == inputs.SEED_A else v * np.float32(0.3)
+
+
+def _big_sample(n, seed=5):
+    rng = np.random.default_rng(seed)
+    edge = np.concatenate([np.arange(4096), np.arange(n - 4096, n),
+                           np.arange((1 << 30) - 2048, (1 << 30) + 2048)])
+    return np.unique(np.concatenate([edge, rng.integers(0, n, 16384)]))
+
+
+def test_streaming_beyond_4gib():
+    n = BIG_N_ROWS * BIG_N_COLS
+    say("stream add, x + c and reduction on %d floats (%.2f GB per array)" % (n, 4e-9 * n))
+    tx, ty = _big_vector(inputs.SEED_A), _big_vector(inputs.SEED_B)
+    idx = _big_sample(n)
+    tidx = torch.from_numpy(idx).to("cuda:0")
+    x, y = _big_vector_at(idx, inputs.SEED_A), _big_vector_at(idx, inputs.SEED_B)
+    assert bits_equal(host(tx[tidx]), x) and bits_equal(host(ty[tidx]), y)
+    z = torch.full_like(tx, float("nan"))
+    pg.pstream_add(tx, ty, z=z)
+    assert bits_equal(host(z[tidx]), oracle.add_f32(x, y))
+    pg.pstream_add_scalar(ty, 1.0, z=z)
+    assert bits_equal(host(z[tidx]), oracle.add_scalar_f32(y, 1.0))
+    del z
+    # (2, h) reductions over the first 2h elements: output j from inputs j and
+    # h + j; h = n/2 (not a multiple of 4: scalar path) and a multiple of 4
+    # (float4 path)
+    for h in (n // 2, n // 8 * 4):
+        say("  reduction (2, %d)" % h)
+        o = pg.preduce_sum_f32(ty[:2 * h].view(2, h))
+        j = idx[idx < h]
+        pair = np.stack([_big_vector_at(j, inputs.SEED_B), _big_vector_at(j + h, inputs.SEED_B)])
+        assert bits_equal(host(o[torch.from_numpy(j).to("cuda:0")]), oracle.sum_axis0_f32(pair))
+
+
 # ------------------------------------------------------------ GEMM, element by element
 
 SMALL_SHAPES = [
