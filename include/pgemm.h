@@ -157,6 +157,25 @@ int pgemm_f16_splitk_default_splits(int64_t M, int64_t N, int64_t K);
 int pgemm_f16_choose_variant(int64_t M, int64_t N, int64_t K);
 
 /*
+ * The launches pgemm_f16 makes for an M x N x K problem on a device with
+ * `cus` compute units (cus <= 0: the current device's count, 256 if it
+ * cannot be read).  Usually one: pgemm_f16_choose_variant's variant over all
+ * M rows (*head_rows = M, *tail_variant = 0).  When that variant uses
+ * 256x256 tiles and their last wave over the CUs would be mostly idle, the
+ * first *head_rows rows (a multiple of 256) run with it and the remaining
+ * M - *head_rows rows with *tail_variant, the 128x128 variant of the same
+ * matrix instruction, which gives bit-identical results.  The split minimises
+ * waves(head tiles) + 0.35 * waves(tail tiles) (a wave of 128x128 tiles
+ * takes about 0.35 of a wave of 256x256 ones at the same K) and is taken
+ * only if it models at least 5% faster, for M*N*K of 1e10 or more.  Pure
+ * host function.  head_rows, head_variant, tail_variant: host pointers,
+ * written on success.  Returns PGEMM_EINVAL for a negative size or a null
+ * pointer, else PGEMM_OK.
+ */
+int pgemm_f16_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* head_rows,
+                   int* head_variant, int* tail_variant);
+
+/*
  * z[i] = x[i] + y[i], i in [0, n): one IEEE binary32 addition per element,
  * round-to-nearest-even, no flush to zero -- bit-identical to any IEEE
  * implementation.  The pipelined elementwise add of the Pallas

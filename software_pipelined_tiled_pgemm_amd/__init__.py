@@ -14,6 +14,7 @@ from ._lib import (PGEMM_EHIP, PGEMM_EINVAL, PGEMM_EUNSUPPORTED, PGEMM_OK, Pgemm
 
 __all__ = [
     "pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants", "pgemm_f16_choose_variant",
+    "pgemm_f16_plan",
     "pgemm_f16_splitk", "pgemm_f16_splitk_workspace_bytes", "pgemm_f16_splitk_default_splits",
     "pstream_add", "pstream_add_blocked", "pstream_add_scalar", "preduce_sum_f32",
     "pgemm_test_fill_f32", "pgemm_test_iota_f32",
@@ -138,6 +139,19 @@ def pgemm_f16_choose_variant(M, N, K):
     if rc < 0:
         raise PgemmError(rc, "pgemm_f16_choose_variant")
     return rc
+
+
+def pgemm_f16_plan(M, N, K, cus=0):
+    """(head_rows, head_variant, tail_variant): the launches pgemm_f16 makes
+    for an M x N x K problem on `cus` CUs (0: the current device's count);
+    tail_variant is 0 when one launch covers all M rows (host only)."""
+    import ctypes
+    head, hv, tv = ctypes.c_int64(), ctypes.c_int(), ctypes.c_int()
+    rc = lib().pgemm_f16_plan(int(M), int(N), int(K), int(cus), ctypes.byref(head),
+                              ctypes.byref(hv), ctypes.byref(tv))
+    if rc < 0:
+        raise PgemmError(rc, "pgemm_f16_plan")
+    return head.value, hv.value, tv.value
 
 
 def _elementwise_out(x, z):

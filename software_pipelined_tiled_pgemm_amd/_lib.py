@@ -35,6 +35,7 @@ def _declare(lib):
         "pgemm_f16_variant": (i32, [p, p, p, i64, i64, i64, i32, p]),
         "pgemm_f16_num_variants": (i32, []),
         "pgemm_f16_choose_variant": (i32, [i64, i64, i64]),
+        "pgemm_f16_plan": (i32, [i64, i64, i64, i32, p, p, p]),
         "pgemm_f16_splitk": (i32, [p, p, p, i64, i64, i64, i32, p, i64, p]),
         "pgemm_f16_splitk_workspace_bytes": (i64, [i64, i64, i64, i32]),
         "pgemm_f16_splitk_default_splits": (i32, [i64, i64, i64]),

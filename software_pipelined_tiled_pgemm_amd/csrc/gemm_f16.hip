@@ -2,6 +2,8 @@
 // shape -> variant chooser; the 16x16x32 family and split-K are in
 // gemm_f16_m16.hip.  The kernels are in gemm_kernels.h.
 
+#include <algorithm>
+
 #include "gemm_kernels.h"
 
 namespace pgemm {
@@ -32,9 +34,10 @@ int gemm_choose_variant(int64_t M, int64_t N, int64_t K) {
     return best;
 }
 
-hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N,
-                           int64_t K, int variant, hipStream_t stream) {
-    if (variant == kGemmAuto) variant = gemm_choose_variant(M, N, K);
+namespace {
+
+hipError_t launch_variant(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                          int variant, hipStream_t stream) {
     float* const nows = nullptr;  // no split-K workspace
     switch (variant) {
         case kGemm256x256: {
@@ -67,6 +70,66 @@ hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int
         default:
             return hipErrorInvalidValue;
     }
+}
+
+}  // namespace
+
+int compute_units() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 256;
+    return cus;
+}
+
+int gemm_small_partner(int variant) {
+    switch (variant) {
+        case kGemm256x256:
+        case kGemm256x256w8:
+            return kGemm128x128;
+        case kGemm256x256w8m16:
+            return kGemm128x128m16;
+        default:
+            return 0;
+    }
+}
+
+int64_t gemm_head_rows(int64_t M, int64_t N, int64_t K, int variant, int cus) {
+    if (gemm_small_partner(variant) == 0 || cus <= 0 || (double)M * N * K < kSplitRowsMinMNK)
+        return M;
+    const int64_t tmb = (M + 255) / 256, tnb = (N + 255) / 256, tns = (N + 127) / 128;
+    auto waves = [cus](int64_t tiles) { return (double)((tiles + cus - 1) / cus); };
+    double best = waves(tmb * tnb) * kSplitRowsMargin;
+    int64_t head = M;
+    // The cost only changes where the head's wave count does: try the
+    // largest head of each wave count.
+    for (int64_t w = 1; (w - 1) * cus < (tmb - 1) * tnb; ++w) {
+        const int64_t r = std::min(tmb - 1, w * cus / tnb);
+        if (r < 1) continue;
+        const int64_t tail_tiles = ((M - 256 * r + 127) / 128) * tns;
+        const double cost = waves(r * tnb) + kSmallTileWave * waves(tail_tiles);
+        if (cost < best) {
+            best = cost;
+            head = 256 * r;
+        }
+    }
+    return head;
+}
+
+hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                           int64_t K, int variant, hipStream_t stream) {
+    if (variant != kGemmAuto) return launch_variant(A, B, C, M, N, K, variant, stream);
+    variant = gemm_choose_variant(M, N, K);
+    const int64_t head = gemm_head_rows(M, N, K, variant, compute_units());
+    if (head >= M) return launch_variant(A, B, C, M, N, K, variant, stream);
+    // Head rows on the 256x256 tile, the rest on the 128x128 tile of the
+    // same matrix-instruction family (bit-identical results, see above).
+    const hipError_t rc = launch_variant(A, B, C, head, N, K, variant, stream);
+    if (rc != hipSuccess) return rc;
+    return launch_variant(static_cast<const _Float16*>(A) + head * K, B,
+                          static_cast<_Float16*>(C) + head * N, M - head, N, K,
+                          gemm_small_partner(variant), stream);
 }
 
 }  // namespace pgemm

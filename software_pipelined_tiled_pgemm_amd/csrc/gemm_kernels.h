@@ -32,7 +32,8 @@
 //    MFMA blocks held in VGPR/AGPR for the whole K loop, zeroed before step 0
 //    (the initialise-before-accumulate rule of the guide, section 7.2).
 //  * Drain (quickstart's epilogue: cast, stage through shared memory, copy
-//    out): fp32 -> fp16, written to LDS, then 16-byte coalesced row stores.
+//    out): fp32 -> fp16, written to LDS, then 16-byte coalesced non-temporal
+//    row stores.
 //
 // Matrix instructions: v_mfma_f32_32x32x16_f16 (variants 1-6: 32x32 output
 // block, 16-deep K, 8 fp16 per lane per operand; lanes 0-31 carry K 0..7,

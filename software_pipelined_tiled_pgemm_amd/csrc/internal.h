@@ -34,8 +34,28 @@ struct TunedShape {
     int variant;
 };
 
+// Variant kGemmAuto runs gemm_choose_variant's pick, except that when its
+// 256x256 tiles would leave most of the last wave of CUs idle it runs the
+// first gemm_head_rows(...) rows with it and the remaining rows with the
+// 128x128 variant of the same matrix instruction (gemm_small_partner): the
+// same results bit for bit, in two launches on the stream.
 hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N,
                            int64_t K, int variant, hipStream_t stream);
+
+// CU count of the current device (256 if it cannot be read).
+int compute_units();
+// The 128x128 variant computing bit-identical results to a 256x256 one, or 0.
+int gemm_small_partner(int variant);
+// Row split for a poorly filled last wave: the head rows (a multiple of 256,
+// or M for no split) minimising the modelled time
+//   waves(head 256x256 tiles) + kSmallTileWave * waves(tail 128x128 tiles),
+// taken only if it beats one launch by the margin; waves = ceil(tiles / cus).
+int64_t gemm_head_rows(int64_t M, int64_t N, int64_t K, int variant, int cus);
+// A wave of 128x128 tiles takes about this fraction of a wave of 256x256
+// tiles at the same K (measured: 42 us against 122 us at K = 6144).
+constexpr double kSmallTileWave = 0.35;
+constexpr double kSplitRowsMargin = 0.95;  // split only for a modelled gain of 5% or more
+constexpr double kSplitRowsMinMNK = 1.0e10;  // below this, launch latency dominates
 // Variants of the 16x16x32 family (gemm_f16_m16.hip).
 hipError_t launch_gemm_f16_m16(const void* A, const void* B, void* C, int64_t M, int64_t N,
                                int64_t K, int variant, hipStream_t stream);

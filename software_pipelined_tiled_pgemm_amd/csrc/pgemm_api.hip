@@ -136,6 +136,18 @@ int pgemm_f16_choose_variant(int64_t M, int64_t N, int64_t K) {
     return pgemm::gemm_choose_variant(M, N, K);
 }
 
+int pgemm_f16_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* head_rows,
+                   int* head_variant, int* tail_variant) {
+    if (M < 0 || N < 0 || K < 0 || !head_rows || !head_variant || !tail_variant)
+        return PGEMM_EINVAL;
+    const int v = pgemm::gemm_choose_variant(M, N, K);
+    const int64_t head = pgemm::gemm_head_rows(M, N, K, v, cus > 0 ? cus : pgemm::compute_units());
+    *head_rows = head;
+    *head_variant = v;
+    *tail_variant = head < M ? pgemm::gemm_small_partner(v) : 0;
+    return PGEMM_OK;
+}
+
 int pstream_add_blocked(const float* x, const float* y, float* z, int64_t n, int64_t block_elems,
                         pgemm_stream_t stream) {
     if (n < 0) return PGEMM_EINVAL;

@@ -23,7 +23,8 @@ def L():
 def test_header_declares_the_boundary():
     names = _lib.declared_functions()
     for n in ["pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants", "pgemm_f16_splitk",
-              "pgemm_f16_splitk_workspace_bytes", "pgemm_f16_choose_variant", "pstream_add",
+              "pgemm_f16_splitk_workspace_bytes", "pgemm_f16_choose_variant", "pgemm_f16_plan",
+              "pstream_add",
               "pstream_add_blocked", "pstream_add_scalar", "pgemm_test_fill_f32",
               "pgemm_test_iota_f32", "preduce_sum_f32", "pgemm_status_string", "pgemm_last_hip_error",
               "pgemm_version"]:

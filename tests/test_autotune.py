@@ -78,3 +78,47 @@ def test_nearest_rule_examples():
     assert autotune.nearest(table, 2048, 2048, 65536) == 2
     assert autotune.nearest(table, 8192, 8192, 8192) == 5
     assert autotune.nearest([], 1, 1, 1) == 2
+
+
+# ------------------------------------------------------------ row split of pgemm_f16
+
+SMALL_PARTNER = {1: 2, 5: 2, 8: 7}  # 256x256 variant -> 128x128 variant of its family
+
+
+def _waves(tiles, cus):
+    return -(-tiles // cus)
+
+
+def test_plan_examples(L):
+    assert pg.pgemm_f16_plan(4096, 4096, 4096, 256) == (4096, 8, 0)  # exactly one wave
+    assert pg.pgemm_f16_plan(8192, 8192, 8192, 256) == (8192, 8, 0)  # exactly four
+    # 6144^3: 576 tiles of 256x256 = 2.25 waves; 21 tile rows (504 tiles, 2
+    # waves) plus 768 rows as 288 tiles of 128x128 (2 waves at 0.35)
+    assert pg.pgemm_f16_plan(6144, 6144, 6144, 256) == (5376, 8, 7)
+    assert pg.pgemm_f16_plan(1024, 1024, 1024, 256)[2] == 0  # too small to split
+
+
+def test_plan_properties_on_random_shapes(L):
+    rng = random.Random(7)
+    for _ in range(400):
+        M, N, K = (rng.choice([8, 128, 256]) * rng.randint(1, 64) for _ in range(3))
+        cus = rng.choice([0, 64, 256, 304])
+        head, hv, tv = pg.pgemm_f16_plan(M, N, K, cus)
+        assert hv == pg.pgemm_f16_choose_variant(M, N, K)
+        if tv == 0:
+            assert head == M
+            continue
+        c = cus or 256
+        assert tv == SMALL_PARTNER[hv] and 0 < head < M and head % 256 == 0
+        assert M * N * K >= 1e10
+        # the split beats one launch by the margin in the library's model
+        whole = _waves(-(-M // 256) * -(-N // 256), c)
+        split = _waves((head // 256) * -(-N // 256), c) + 0.35 * _waves(-(-(M - head) // 128) * -(-N // 128), c)
+        assert split < 0.95 * whole, (M, N, K, cus, head)
+
+
+def test_plan_argument_errors(L):
+    import ctypes
+    h, a, b = ctypes.c_int64(), ctypes.c_int(), ctypes.c_int()
+    assert L.pgemm_f16_plan(-1, 8, 8, 256, ctypes.byref(h), ctypes.byref(a), ctypes.byref(b)) == pg.PGEMM_EINVAL
+    assert L.pgemm_f16_plan(8, 8, 8, 256, None, ctypes.byref(a), ctypes.byref(b)) == pg.PGEMM_EINVAL

@@ -411,6 +411,30 @@ def test_gemm_full_size_sampled(name, M, N, K, dist):
     say("  sample %d points: max |ulp diff| %d, frac exact %.4f" % (I.size, d.max(), np.mean(d == 0)))
 
 
+# ------------------------------------------------------------ automatic row split
+
+# Shapes whose 256x256 tiles leave most of the last wave idle: pgemm_f16 runs
+# the head rows with the 256x256 variant and the rest with the 128x128
+# variant of the same family.  The result must be bit-identical to the
+# 256x256 variant over all rows, and within the bound of the oracle.
+ROW_SPLIT_CASES = [(4392, 4352, 4096), (6144, 6144, 6144)]
+
+
+@pytest.mark.parametrize("M,N,K", ROW_SPLIT_CASES)
+def test_gemm_auto_row_split(M, N, K):
+    head, hv, tv = pg.pgemm_f16_plan(M, N, K)
+    say("gemm auto %dx%dx%d: head %d rows on variant %d, tail on variant %d" % (M, N, K, head, hv, tv))
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert 0 < head < M and tv != 0, "the split should be taken on 256 CUs"
+    A, B = inputs.gemm_inputs(M, N, K)
+    tA, tB = dev(A), dev(B)
+    auto = gemm(tA, tB)
+    assert bits_equal(auto, gemm(tA, tB, hv))
+    I, J = inputs.sample_points(M, N, 4096, seed=6, full_rows=8, full_cols=8)
+    ref, _ = oracle.gemm_f16_points(A, B, I, J)
+    assert_close(auto[I, J], ref, "auto %dx%dx%d" % (M, N, K))
+
+
 # ------------------------------------------------------------ one GPU's row shard
 
 # Split G ways by rows of C, GPU g computes A's row block g times all of B
