@@ -167,8 +167,10 @@ int pgemm_f16_choose_variant(int64_t M, int64_t N, int64_t K);
  * matrix instruction, which gives bit-identical results.  The split minimises
  * waves(head tiles) + 0.35 * waves(tail tiles) (a wave of 128x128 tiles
  * takes about 0.35 of a wave of 256x256 ones at the same K) and is taken
- * only if it models at least 5% faster, for M*N*K of 1e10 or more.  Pure
- * host function.  head_rows, head_variant, tail_variant: host pointers,
+ * only if it models at least 5% faster, for M*N*K of 1e10 or more.  Host
+ * function: with cus > 0 it makes no HIP call; with cus <= 0 its only HIP
+ * calls read the current device's attribute.  head_rows, head_variant,
+ * tail_variant: host pointers,
  * written on success.  Returns PGEMM_EINVAL for a negative size or a null
  * pointer, else PGEMM_OK.
  */
