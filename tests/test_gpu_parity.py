@@ -1,7 +1,8 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
 Bars: bit-exact for the streaming add, x + c, fill and iota; for the GEMM
-|gpu - oracle| <= 5e-3 * (|oracle| + 1) per element on inputs in [-1, 1],
+|gpu - oracle| <= 5e-3 * (|oracle| + 1) per element on inputs in [-1, 1]
+(and, tighter, the a-priori bound of fp32 accumulation: assert_fp32_bound),
 bit-exact where the exact result is an fp16 value that fp32 accumulation
 reaches exactly (identity, ones, power-of-two rank-1).  Full-size GEMMs are
 checked on a deterministic sample of outputs computed one by one by the
@@ -16,6 +17,7 @@ import oracle
 import software_pipelined_tiled_pgemm_amd as pg
 from software_pipelined_tiled_pgemm_amd import inputs
 from tests import _golden
+from tests._bounds import fp32_bound_violations, ulp16  # noqa: F401
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -60,6 +62,12 @@ def assert_close(got, ref, what=""):
         idx = np.argwhere(~ok)[:8]
         detail = ", ".join("%s: gpu %r oracle %r" % (tuple(i), g[tuple(i)], r[tuple(i)]) for i in idx)
         pytest.fail("%s: %d of %d outside tolerance; first: %s" % (what, (~ok).sum(), ok.size, detail))
+
+
+def assert_fp32_bound(got, ref, Sabs, K, what=""):
+    bad = fp32_bound_violations(got, ref, Sabs, K)
+    if bad.any():
+        pytest.fail("%s: %d of %d outside the fp32 accumulation bound" % (what, bad.sum(), bad.size))
 
 
 def bits_equal(a, b):
@@ -264,10 +272,12 @@ SMALL_SHAPES = [
 def test_gemm_small_shapes_vs_full_oracle(M, N, K):
     A, B = inputs.gemm_inputs(M, N, K)
     ref, _ = oracle.gemm_f16(A, B)
+    _, Sabs = oracle.gemm_f16(np.abs(A), np.abs(B))
     outs = {}
     for v in VARIANTS:
         got = gemm(A, B, v)
         assert_close(got, ref, "M=%d N=%d K=%d variant %d" % (M, N, K, v))
+        assert_fp32_bound(got, ref, Sabs, K, "M=%d N=%d K=%d variant %d" % (M, N, K, v))
         outs[v] = got
     # inside a family the K order of an element depends neither on the tile
     # size nor on the pipeline (LDS-DMA ring vs register staging): any
@@ -409,6 +419,10 @@ def test_gemm_full_size_sampled(name, M, N, K, dist):
     # diagnostics on the sample: error in fp16 ulps of the oracle value
     d = np.abs(got[I, J].view(np.uint16).astype(np.int64) - ref.view(np.uint16).astype(np.int64))
     say("  sample %d points: max |ulp diff| %d, frac exact %.4f" % (I.size, d.max(), np.mean(d == 0)))
+    g = got[I, J].astype(np.float64)
+    say("  relative Frobenius error against the exact sums: %.3e" % (np.linalg.norm(g - S) / np.linalg.norm(S)))
+    _, Sabs = oracle.gemm_f16_points(np.abs(A), np.abs(B), I, J)
+    assert_fp32_bound(got[I, J], ref, Sabs, K, name)
 
 
 # ------------------------------------------------------------ automatic row split
@@ -520,8 +534,10 @@ SPLITK_CASES = [(64, 64, 512, 2), (200, 136, 1000, 3), (256, 256, 4096, 4), (300
 def test_gemm_splitk_vs_full_oracle(M, N, K, splits):
     A, B = inputs.gemm_inputs(M, N, K)
     ref, _ = oracle.gemm_f16(A, B)
+    _, Sabs = oracle.gemm_f16(np.abs(A), np.abs(B))
     got = splitk(A, B, splits)
     assert_close(got, ref, "split-K %dx%dx%d/%d" % (M, N, K, splits))
+    assert_fp32_bound(got, ref, Sabs, K, "split-K %dx%dx%d/%d" % (M, N, K, splits))
     assert bits_equal(got, splitk(A, B, splits)), "split-K is not deterministic"
 
 
@@ -561,6 +577,8 @@ def test_gemm_splitk_full_size_sampled():
     I, J = inputs.sample_points(M, N, 8192)
     ref, _ = oracle.gemm_f16_points(A, B, I, J)
     assert_close(got[I, J], ref, "split-K long K")
+    _, Sabs = oracle.gemm_f16_points(np.abs(A), np.abs(B), I, J)
+    assert_fp32_bound(got[I, J], ref, Sabs, K, "split-K long K")
 
 
 def test_gemm_splitk_device_argument_checks():

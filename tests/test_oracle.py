@@ -393,3 +393,43 @@ def test_sum_axis0_order_pin_rejects_other_orders(mutant):
     x = np.array([[1.0], [e], [e], [e], [e]], np.float32)
     assert oracle.sum_axis0_f32(x)[0] == np.float32(1.0)
     assert mutant(x)[0] != np.float32(1.0)
+
+
+# ------------------------------------------------------------ the fp32 accumulation bound
+
+def _fp32_sums(A, B, order):
+    """fp16 GEMM with fp32 accumulation in a given order, simulated on the host."""
+    P = A.astype(np.float32)[:, :, None] * B.astype(np.float32)[None, :, :]  # exact products
+    if order == "ascending":
+        return np.cumsum(P, axis=1, dtype=np.float32)[:, -1, :]
+    if order == "descending":
+        return np.cumsum(P[:, ::-1, :], axis=1, dtype=np.float32)[:, -1, :]
+    # blocks of 32 products summed pairwise, blocks added in ascending order
+    K = P.shape[1]
+    blocks = np.add.reduce(P.reshape(P.shape[0], K // 32, 32, P.shape[2]), axis=2, dtype=np.float32)
+    return np.cumsum(blocks, axis=1, dtype=np.float32)[:, -1, :]
+
+
+@pytest.mark.parametrize("K", [64, 1024, 4096])
+def test_fp32_bound_holds_for_any_order_and_catches_mistakes(K):
+    from software_pipelined_tiled_pgemm_amd import inputs
+    from tests._bounds import fp32_bound_violations
+    A, B = inputs.gemm_inputs(48, 40, K, seed_a=30, seed_b=31)
+    ref, _ = oracle.gemm_f16(A, B)
+    _, Sabs = oracle.gemm_f16(np.abs(A), np.abs(B))
+    for order in ("ascending", "descending", "blocks"):
+        got = _fp32_sums(A, B, order).astype(np.float16)
+        assert not fp32_bound_violations(got, ref, Sabs, K).any(), order
+    # plausible kernel mistakes must fall outside it for most outputs; the
+    # bound grows like K * 2**-24 * K/4, so one dropped term (|ab| ~ 1/4)
+    # stands out only up to K of about a thousand
+    if K <= 1024:
+        dropped = _fp32_sums(A[:, 1:], B[1:, :], "ascending")
+        assert fp32_bound_violations(dropped.astype(np.float16), ref, Sabs, K).mean() > 0.5
+    half_k = _fp32_sums(A[:, : K // 2], B[: K // 2, :], "ascending")
+    assert fp32_bound_violations(half_k.astype(np.float16), ref, Sabs, K).mean() > 0.9
+    transposed_b = _fp32_sums(A[:, :40], B[:40, :].T.copy(), "ascending") if K == 64 else None
+    if transposed_b is not None:
+        ref40, _ = oracle.gemm_f16(A[:, :40], B[:40, :])
+        _, Sabs40 = oracle.gemm_f16(np.abs(A[:, :40]), np.abs(B[:40, :]))
+        assert fp32_bound_violations(transposed_b.astype(np.float16), ref40, Sabs40, 40).mean() > 0.9
