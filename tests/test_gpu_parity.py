@@ -653,3 +653,52 @@ def test_autotune_measures_every_variant():
     assert all(x > 0 for x in recs[0]["tflops"].values())
     table = autotune.parse_table(autotune.render_table(recs, "test"))
     assert table == [(256, 256, 256, autotune.fastest(recs[0]))]
+
+
+# ------------------------------------------------------------ HIP graph capture
+
+def test_graph_capture_and_replay():
+    # Every call only enqueues kernels on the caller's stream (no allocation,
+    # no synchronisation, no memset), so a captured sequence replays.  Each
+    # replay follows eager work that poisons the outputs and is checked
+    # against the eager results.
+    say("graph capture: gemm (auto, row split), split-K, stream add, x + c, reduction")
+    A, B = inputs.gemm_inputs(4392, 4352, 4096)
+    tA, tB = dev(A), dev(B)
+    A2, B2 = inputs.gemm_inputs(256, 264, 8192, seed_a=60, seed_b=61)
+    tA2, tB2 = dev(A2), dev(B2)
+    x, y = inputs.stream_inputs(1 << 22, 62, 63)
+    tx, ty = dev(x), dev(y)
+    r = dev(inputs.uniform_f32((6, 1 << 18), 64))
+    C = torch.empty((4392, 4352), dtype=torch.float16, device="cuda:0")
+    C2 = torch.empty((256, 264), dtype=torch.float16, device="cuda:0")
+    W = torch.empty(pg.pgemm_f16_splitk_workspace_bytes(256, 264, 8192, 4) // 4, device="cuda:0")
+    z = torch.empty_like(tx)
+    z1 = torch.empty_like(tx)
+    o = torch.empty(1 << 18, device="cuda:0")
+
+    def work():
+        pg.pgemm_f16(tA, tB, C=C)
+        pg.pgemm_f16_splitk(tA2, tB2, 4, C=C2, workspace=W)
+        pg.pstream_add(tx, ty, z=z)
+        pg.pstream_add_scalar(tx, 1.0, z=z1)
+        pg.preduce_sum_f32(r, out=o)
+
+    outs = (C, C2, z, z1, o)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()  # eager run on a side stream (also the warm-up before capture)
+    torch.cuda.current_stream().wait_stream(s)
+    eager = [host(t).copy() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        for t, e in zip(outs, eager):
+            assert bits_equal(host(t), e), "replay %d" % rep
+    assert bits_equal(eager[2], oracle.add_f32(x, y))
