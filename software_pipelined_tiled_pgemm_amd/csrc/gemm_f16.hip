@@ -124,7 +124,8 @@ hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int
     const int64_t head = gemm_head_rows(M, N, K, variant, compute_units());
     if (head >= M) return launch_variant(A, B, C, M, N, K, variant, stream);
     // Head rows on the 256x256 tile, the rest on the 128x128 tile of the
-    // same matrix-instruction family (bit-identical results, see above).
+    // same matrix-instruction family: every output's K sum is grouped the
+    // same way, so the results are bit-identical to one launch.
     const hipError_t rc = launch_variant(A, B, C, head, N, K, variant, stream);
     if (rc != hipSuccess) return rc;
     return launch_variant(static_cast<const _Float16*>(A) + head * K, B,
