@@ -265,6 +265,12 @@ SMALL_SHAPES = [
     (264, 136, 416),   # 13 steps: no unrolled pass, odd step count
     (256, 256, 480),   # 15 steps
     (128, 384, 832),   # 26 steps: two unrolled passes, a run-time one, tail
+    # extreme aspect ratios: one row, the narrowest C, one tile row/column
+    # with long K
+    (1, 8192, 4096),
+    (8192, 8, 4096),
+    (3, 4104, 1032),
+    (4100, 24, 2056),
 ]
 
 
