@@ -293,6 +293,35 @@ def test_gemm_small_shapes_vs_full_oracle(M, N, K):
             assert bits_equal(outs[fam[0]], outs[v]), "variants %d and %d differ" % (fam[0], v)
 
 
+def test_gemm_special_values_all_variants():
+    # Not part of any benchmark input, but IEEE semantics must hold: NaN
+    # where the exact sum is undefined, +-inf where it overflows fp16 or
+    # includes an infinite product, the rest within the bounds.
+    M, N, K = 136, 144, 264
+    say("gemm with NaN, +-inf and fp16-overflowing sums, %dx%dx%d" % (M, N, K))
+    A, B = inputs.gemm_inputs(M, N, K, seed_a=70, seed_b=71)
+    A, B = A.copy(), B.copy()
+    A[3, 10] = np.inf
+    A[5, 20] = np.nan
+    B[30, 7] = -np.inf
+    A[9, :] = 300.0   # row 9 times column 11 sums to 264 * 90000: fp16 overflow
+    B[:, 11] = 300.0
+    B[:, 12] = -300.0
+    ref, _ = oracle.gemm_f16(A, B)
+    r = ref.astype(np.float64)
+    special = ~np.isfinite(r)
+    assert np.isnan(r).sum() > 0 and np.isposinf(r).sum() > 0 and np.isneginf(r).sum() > 0
+    _, Sabs = oracle.gemm_f16(np.abs(A), np.abs(B))
+    for v in VARIANTS:
+        got = gemm(A, B, v).astype(np.float64)
+        assert np.array_equal(np.isnan(got), np.isnan(r)), "variant %d: NaN positions" % v
+        inf = np.isinf(r)
+        assert np.array_equal(got[inf], r[inf]), "variant %d: infinities" % v
+        fin = ~special
+        assert_close(got[fin], r[fin], "variant %d finite part" % v)
+        assert_fp32_bound(got[fin], r[fin], Sabs[fin], K, "variant %d finite part" % v)
+
+
 @pytest.mark.parametrize("v", VARIANTS)
 def test_gemm_k_zero_gives_zeros(v):
     say("gemm K=0")
