@@ -669,6 +669,21 @@ def test_sum_axis0_order_and_empty():
     assert np.array_equal(z.view(np.uint32), np.zeros(8, np.uint32))
 
 
+@pytest.mark.parametrize("n", [1024, 1022])  # float4 path, scalar path
+def test_sum_axis0_special_values(n):
+    # ordered triples of the special values down the reduction axis:
+    # signed zeros, subnormals, infinities (inf + -inf = NaN), NaN, overflow
+    say("sum axis 0 special values, n=%d" % n)
+    sp = SPECIAL.astype(np.float32)
+    trip = np.array(np.meshgrid(sp, sp, sp, indexing="ij")).reshape(3, -1)  # 3 x 3375
+    x = np.ascontiguousarray(trip[:, np.random.default_rng(5).permutation(trip.shape[1])[:n]])
+    got = host(pg.preduce_sum_f32(dev(x)))
+    ref = oracle.sum_axis0_f32(x)
+    nan = np.isnan(ref)
+    assert nan.any() and np.array_equal(np.isnan(got), nan)
+    assert bits_equal(got[~nan], ref[~nan])
+
+
 def test_sum_axis0_misaligned_view_scalar_path():
     say("sum axis 0 misaligned")
     R, n = 5, 1001
