@@ -209,6 +209,22 @@ def cpu_baseline(inputs, target_seconds):
                       % (rows, t, cores)}
 
 
+def cpu_baseline_stream(inputs):
+    """The oracle's elementwise add (plain loop, all host threads) on the
+    same 8192 x 8192 workload, 5 calls after one untimed one, in GB/s of
+    12 algorithmic bytes per element."""
+    import oracle
+    x, y = inputs.stream_inputs((8192, 8192))
+    oracle.add_f32(x, y)
+    t0 = time.perf_counter()
+    for _ in range(5):
+        oracle.add_f32(x, y)
+    t = (time.perf_counter() - t0) / 5
+    return {"value": round(12.0 * x.size / t / 1e9, 2), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle", "sample": "the full 8192x8192 add, 5 calls (%.3f s each, %d threads)"
+            % (t, oracle.threads())}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -297,6 +313,8 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)
+        if "streaming" in out:
+            out["streaming"]["cpu_baseline"] = cpu_baseline_stream(inputs)
     print(json.dumps(out), flush=True)
 
 
