@@ -5,13 +5,25 @@ MI355X.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
 
 A step is one GEMM launch at 4096^3 on inputs already resident in HBM.  The
-timed region is exactly K steps on one stream, bracketed by device
-synchronisation, and timed with HIP events recorded on that stream.  The
-default warm-up (300 launches) lets the clock settle: throughput rises over
-the first ~200 launches of a cold process and is flat afterwards.  The
-streaming kernels get their own timed regions of K launches each (rotating
-over three buffer sets, so no launch re-reads what the previous one left in
-the caches).  Prints one JSON line.
+timed region is exactly K steps on one stream after W untimed warm-up
+steps, bracketed by device synchronisation and timed with HIP events
+recorded on that stream.  Prints one JSON line.
+
+Order of the run.  Every input of every leg is generated and copied to the
+device first, so that no host work leaves the GPU idle between the legs.
+Then:
+  1. cold_start: the 4096^3 GEMM, W + K launches, the first GPU work of the
+     process.  MI355X runs at its 1400 W power cap under this GEMM; after
+     idle its power controller first lets the clock run, then throttles
+     hard for about 10 ms before it settles (per-launch durations of
+     100 -> 130 -> 98 us), so a short run here times that transient.
+  2. the secondary legs (streaming add at the default and at the pages'
+     512 x 512 blocks, x + 1, the reduction, the other GEMM configurations),
+     each after a settle phase of back-to-back launches lasting at least
+     --settle-ms, then W warm-up and K timed launches of its own;
+  3. the headline: W warm-up and K timed launches of the 4096^3 GEMM,
+     right after the 8192^3 leg, i.e. at the sustained clock of a busy GPU.
+`value` is (3); the cold figure is reported beside it.
 """
 from __future__ import annotations
 
@@ -37,23 +49,27 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="back-to-back launches before each secondary leg's warm-up")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
     ap.add_argument("--quick", action="store_true", help="headline GEMM only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle sample")
+                    help="target CPU time of the headline oracle sample")
     ap.add_argument("--profile", action="store_true",
                     help="no timing: a 512 MiB device copy (counter calibration) followed by "
-                         "3 launches of each kernel, for rocprofv3 runs")
+                         "launches of each kernel, for rocprofv3 runs")
+    ap.add_argument("--profile-reps", type=int, default=3,
+                    help="launches of each kernel in --profile mode")
     return ap.parse_args()
 
 
-def profile_run(pg, inputs):
+def profile_run(pg, inputs, reps):
     """Launch sequence for counter collection: one plain copy of known size
     (512 MiB read + 512 MiB written) to calibrate FETCH_SIZE / WRITE_SIZE,
-    then 3 launches each of the 4096^3 GEMM, the streaming add, x + 1 and the
-    (8, 4096, 4096) reduction."""
+    then `reps` launches each of the 4096^3 GEMM, the streaming add, x + 1
+    and the (8, 4096, 4096) reduction."""
     import torch
     src = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -66,16 +82,16 @@ def profile_run(pg, inputs):
     x, y = inputs.stream_inputs((8192, 8192))
     tx, ty = torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()
     tz = torch.empty_like(tx)
-    for _ in range(3):
+    for _ in range(reps):
         pg.pgemm_f16(tA, tB, C=tC)
-    for _ in range(3):
+    for _ in range(reps):
         pg.pstream_add(tx, ty, z=tz)
-    for _ in range(3):
+    for _ in range(reps):
         pg.pstream_add_scalar(tx, 1.0, z=tz)
     del tx, ty, tz
     xr = torch.from_numpy(inputs.uniform_f32((8, 4096, 4096), 0)).cuda()
     o = torch.empty((4096, 4096), dtype=torch.float32, device="cuda")
-    for _ in range(3):
+    for _ in range(reps):
         pg.preduce_sum_f32(xr, out=o)
     torch.cuda.synchronize()
     print("profile launches done", flush=True)
@@ -104,8 +120,26 @@ def measured_traffic(kernel, src_hash):
     return ent.get("bytes_per_launch")
 
 
-def time_launches(fn, steps, warmup, stream):
+def settle(fn, seconds):
+    """Back-to-back launches of fn until `seconds` have passed (in batches
+    of 10, synchronised); returns the number of launches."""
     import torch
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for i in range(10):
+            fn(n + i)
+        n += 10
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
+def time_launches(fn, steps, warmup, stream, settle_s=0.0):
+    """Seconds for `steps` launches of fn after `warmup` untimed ones (and,
+    before those, `settle_s` seconds of back-to-back launches)."""
+    import torch
+    settled = settle(fn, settle_s) if settle_s > 0 else 0
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -116,15 +150,21 @@ def time_launches(fn, steps, warmup, stream):
         fn(i)
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3  # seconds
+    return start.elapsed_time(end) / 1e3, settled
 
 
-def gemm_case(pg, inputs, M, N, K, dist, steps, warmup, stream, splitk=False):
+def gemm_operands(inputs, M, N, K, dist):
     import torch
     A, B = inputs.gemm_inputs(M, N, K, dist)
-    tA = torch.from_numpy(A).cuda()
-    tB = torch.from_numpy(B).cuda()
-    tC = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    return (torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(),
+            torch.empty((M, N), dtype=torch.float16, device="cuda"))
+
+
+def gemm_case(pg, ops, dist, steps, warmup, stream, settle_s=0.0, splitk=False):
+    import torch
+    tA, tB, tC = ops
+    M, K = tA.shape
+    N = tB.shape[1]
     rec = {"M": M, "N": N, "K": K, "dist": dist}
     if splitk:
         splits = pg.pgemm_f16_splitk_default_splits(M, N, K)
@@ -136,49 +176,58 @@ def gemm_case(pg, inputs, M, N, K, dist, steps, warmup, stream, splitk=False):
     else:
         fn = lambda i: pg.pgemm_f16(tA, tB, C=tC)
         rec["path"] = "pgemm_f16 (variant %d)" % pg.pgemm_f16_choose_variant(M, N, K)
-    secs = time_launches(fn, steps, warmup, stream)
-    flops = 2.0 * M * N * K
-    tflops = flops * steps / secs / 1e12
+    secs, settled = time_launches(fn, steps, warmup, stream, settle_s)
+    tflops = 2.0 * M * N * K * steps / secs / 1e12
     rec.update({"us_per_launch": secs / steps * 1e6, "tflops": tflops,
-                "frac_of_peak": tflops / PEAK_FP16_TFLOPS})
+                "frac_of_peak": tflops / PEAK_FP16_TFLOPS, "settle_launches": settled,
+                "warmup": warmup, "steps": steps})
     return rec
 
 
-def stream_case(pg, inputs, steps, warmup, stream, scalar):
-    import torch
-    n = 8192 * 8192
-    x, y = inputs.stream_inputs((8192, 8192))
-    sets = []
-    for _ in range(3):
-        sets.append((torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda(),
-                     torch.empty(n, dtype=torch.float32, device="cuda")))
-    if scalar:
+def stream_case(pg, sets, steps, warmup, stream, settle_s, kind, block=None):
+    n = sets[0][0].numel()
+    if kind == "scalar":
         fn = lambda i: pg.pstream_add_scalar(sets[i % 3][0], 1.0, z=sets[i % 3][2])
         bytes_per = 8.0 * n
+    elif block is not None:
+        fn = lambda i: pg.pstream_add_blocked(sets[i % 3][0], sets[i % 3][1], block,
+                                              z=sets[i % 3][2])
+        bytes_per = 12.0 * n
     else:
         fn = lambda i: pg.pstream_add(sets[i % 3][0], sets[i % 3][1], z=sets[i % 3][2])
         bytes_per = 12.0 * n
-    secs = time_launches(fn, steps, warmup, stream)
+    secs, settled = time_launches(fn, steps, warmup, stream, settle_s)
     gbs = bytes_per * steps / secs / 1e9
-    return {"n": n, "bytes_per_launch": bytes_per, "us_per_launch": secs / steps * 1e6,
-            "GB/s": gbs, "frac_of_hbm": gbs / PEAK_HBM_GBS}
+    return {"bytes_per_launch": bytes_per, "us_per_launch": round(secs / steps * 1e6, 2),
+            "value": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "settle_launches": settled}
 
 
-def reduce_case(pg, inputs, steps, warmup, stream):
+def reduce_case(pg, sets, out, steps, warmup, stream, settle_s):
     """The guide's section 7.2 reduction at (8, 4096, 4096) f32: 8 slices of
     64 MiB summed over the first axis; 9 * 64 MiB move per launch."""
-    import torch
-    R, M, N = 8, 4096, 4096
-    sets = [torch.from_numpy(inputs.uniform_f32((R, M, N), s)).cuda() for s in (0, 1)]
-    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    secs = time_launches(lambda i: pg.preduce_sum_f32(sets[i % 2], out=out), steps, warmup, stream)
+    R, M, N = sets[0].shape
+    secs, settled = time_launches(lambda i: pg.preduce_sum_f32(sets[i % 2], out=out), steps,
+                                  warmup, stream, settle_s)
     bytes_per = 4.0 * (R + 1) * M * N
     gbs = bytes_per * steps / secs / 1e9
     return {"workload": "sum over axis 0 of (8, 4096, 4096) f32, U[-1,1], 2 rotating inputs",
             "value": round(gbs, 1), "unit": "GB/s", "us_per_launch": round(secs / steps * 1e6, 2),
+            "settle_launches": settled,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic("sum_axis0_vec_kernel", kernel_source_hash())}}
+
+
+# ------------------------------------------------------------------ CPU baselines
+
+def _oracle_points_rate(oracle, A, B, I, J):
+    """(seconds, multiply-adds per second) of the oracle on sampled outputs."""
+    K = A.shape[1]
+    t0 = time.perf_counter()
+    oracle.gemm_f16_points(A, B, I, J)
+    t = time.perf_counter() - t0
+    return t, I.size * K / t
 
 
 def cpu_baseline(inputs, target_seconds):
@@ -209,20 +258,52 @@ def cpu_baseline(inputs, target_seconds):
                       % (rows, t, cores)}
 
 
-def cpu_baseline_stream(inputs):
-    """The oracle's elementwise add (plain loop, all host threads) on the
-    same 8192 x 8192 workload, 5 calls after one untimed one, in GB/s of
-    12 algorithmic bytes per element."""
+def cpu_baselines_other(inputs):
+    """The oracle on the other configurations: 256^3 in full on one thread
+    and on all threads; 8192^3 and 2048^2 x 32768 on the deterministic
+    output sample the parity tests use (32 rows, 32 columns, 8192 points,
+    the corners of every 128-tile), extrapolated to the whole product by the
+    per-output time and labelled as such; the streaming add on the full
+    8192^2 workload on one thread and on all threads."""
     import oracle
+    allc = oracle.threads()
+    out = []
+    A, B = inputs.gemm_inputs(256, 256, 256)
+    for th in (1, allc):
+        oracle.set_threads(th)
+        oracle.gemm_f16(A, B)  # first call builds the decode table
+        t0 = time.perf_counter()
+        oracle.gemm_f16(A, B)
+        t = time.perf_counter() - t0
+        out.append({"workload": "GEMM 256^3, full product", "value": 2.0 * 256 ** 3 / t / 1e12,
+                    "unit": "TFLOP/s", "seconds": t, "cores": th, "kind": "oracle"})
+    oracle.set_threads(allc)
+    for (M, N, K, dist) in [(8192, 8192, 8192, "normal"), (2048, 2048, 32768, "uniform")]:
+        A, B = inputs.gemm_inputs(M, N, K, dist)
+        I, J = inputs.sample_points(M, N, 8192)
+        t, rate = _oracle_points_rate(oracle, A, B, I, J)
+        full = M * N * K / rate
+        out.append({"workload": "GEMM %dx%dx%d %s" % (M, N, K, dist),
+                    "value": 2.0 * rate / 1e12, "unit": "TFLOP/s", "cores": allc, "kind": "oracle",
+                    "sample": "%d sampled outputs in %.2f s" % (I.size, t),
+                    "extrapolated_full_seconds": round(full, 1),
+                    "note": "extrapolated from the sample by time per output"})
     x, y = inputs.stream_inputs((8192, 8192))
-    oracle.add_f32(x, y)
-    t0 = time.perf_counter()
-    for _ in range(5):
+    for th in (1, allc):
+        oracle.set_threads(th)
         oracle.add_f32(x, y)
-    t = (time.perf_counter() - t0) / 5
-    return {"value": round(12.0 * x.size / t / 1e9, 2), "unit": "GB/s", "cores": oracle.threads(),
-            "kind": "oracle", "sample": "the full 8192x8192 add, 5 calls (%.3f s each, %d threads)"
-            % (t, oracle.threads())}
+        t0 = time.perf_counter()
+        for _ in range(3):
+            oracle.add_f32(x, y)
+        t = (time.perf_counter() - t0) / 3
+        out.append({"workload": "streaming add 8192^2 fp32, full", "value": round(12.0 * x.size / t / 1e9, 2),
+                    "unit": "GB/s", "seconds": t, "cores": th, "kind": "oracle"})
+    oracle.set_threads(allc)
+    for r in out:
+        for k, v in list(r.items()):
+            if isinstance(v, float):
+                r[k] = round(v, 6)
+    return out
 
 
 def main():
@@ -244,26 +325,86 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     if args.profile:
-        profile_run(pg, inputs)
+        profile_run(pg, inputs, args.profile_reps)
         return
     stream = torch.cuda.current_stream()
     props = torch.cuda.get_device_properties(0)
     print("device: %s, %d CUs; assumed peaks: fp16 MFMA %.1f TFLOP/s, HBM %.0f GB/s"
           % (props.name, props.multi_processor_count, PEAK_FP16_TFLOPS, PEAK_HBM_GBS),
           file=sys.stderr, flush=True)
+    W, K = args.warmup, args.steps
+    settle_s = args.settle_ms / 1e3
 
-    head = gemm_case(pg, inputs, 4096, 4096, 4096, "uniform", args.steps, args.warmup, stream)
+    # Every input on the device before the first timed leg.
+    head_ops = gemm_operands(inputs, 4096, 4096, 4096, "uniform")
+    if not args.quick:
+        x, y = inputs.stream_inputs((8192, 8192))
+        sets = [(torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda(),
+                 torch.empty(x.size, dtype=torch.float32, device="cuda")) for _ in range(3)]
+        sets = [(a.view(-1), b.view(-1), c) for a, b, c in sets]
+        del x, y
+        red_sets = [torch.from_numpy(inputs.uniform_f32((8, 4096, 4096), s)).cuda() for s in (0, 1)]
+        red_out = torch.empty((4096, 4096), dtype=torch.float32, device="cuda")
+        other_ops = [(M, N, Kk, dist, gemm_operands(inputs, M, N, Kk, dist))
+                     for (M, N, Kk, dist) in [(256, 256, 256, "uniform"),
+                                              (2048, 2048, 32768, "uniform"),
+                                              (8192, 8192, 8192, "normal")]]
+    torch.cuda.synchronize()
+
+    cold = gemm_case(pg, head_ops, "uniform", K, W, stream)
+    print("gemm 4096^3, cold start: %.1f us, %.1f TFLOP/s" % (cold["us_per_launch"], cold["tflops"]),
+          file=sys.stderr, flush=True)
+
+    out_extra = {}
+    if not args.quick:
+        add = stream_case(pg, sets, K, W, stream, settle_s, "add")
+        add512 = stream_case(pg, sets, K, W, stream, settle_s, "add", block=512 * 512)
+        addc = stream_case(pg, sets, K, W, stream, settle_s, "scalar")
+        print("stream add: %.1f GB/s (512x512 blocks %.1f); x+1: %.1f GB/s"
+              % (add["value"], add512["value"], addc["value"]), file=sys.stderr, flush=True)
+        src_hash = kernel_source_hash()
+        out_extra["streaming"] = {
+            "workload": "z = x + y, fp32 8192x8192, U[-1,1], 3 rotating buffer sets",
+            "value": add["value"], "unit": "GB/s", "us_per_launch": add["us_per_launch"],
+            "block_elems": 4096, "settle_launches": add["settle_launches"],
+            "roofline": {"bound": "hbm", "achieved": add["value"], "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": add["frac"],
+                         "traffic": measured_traffic("add_vec_kernel", src_hash)},
+            "blocks_512x512": {"value": add512["value"], "unit": "GB/s",
+                               "us_per_launch": add512["us_per_launch"], "frac": add512["frac"],
+                               "block_elems": 512 * 512,
+                               "note": "pstream_add_blocked with the pages' 512x512 blocks"},
+            "x_plus_1": {"value": addc["value"], "unit": "GB/s",
+                         "us_per_launch": addc["us_per_launch"], "frac": addc["frac"]},
+        }
+        out_extra["reduction"] = reduce_case(pg, red_sets, red_out, K, W, stream, settle_s)
+        print("reduction: %.1f GB/s" % out_extra["reduction"]["value"], file=sys.stderr, flush=True)
+        del sets, red_sets, red_out
+        others = []
+        for (M, N, Kk, dist, ops) in other_ops:
+            r = gemm_case(pg, ops, dist, K, W, stream, settle_s)
+            print("gemm %dx%dx%d: %.1f us, %.1f TFLOP/s" % (M, N, Kk, r["us_per_launch"], r["tflops"]),
+                  file=sys.stderr, flush=True)
+            others.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+            if (M, N, Kk) == (2048, 2048, 32768):
+                # long K through split-K (the caller provides the fp32 workspace)
+                r = gemm_case(pg, ops, dist, K, W, stream, settle_s, splitk=True)
+                print("gemm %dx%dx%d split-K: %.1f us, %.1f TFLOP/s"
+                      % (M, N, Kk, r["us_per_launch"], r["tflops"]), file=sys.stderr, flush=True)
+                others.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+        out_extra["other_gemm"] = others
+
+    head = gemm_case(pg, head_ops, "uniform", K, W, stream)
     print("gemm 4096^3: %.1f us, %.1f TFLOP/s" % (head["us_per_launch"], head["tflops"]),
           file=sys.stderr, flush=True)
-    src_hash = kernel_source_hash()
-    traffic = measured_traffic("gemm_f16_kernel_4096", src_hash)
+    traffic = measured_traffic("gemm_f16_kernel_4096", kernel_source_hash())
     out = {
         "metric": METRIC,
         "value": round(head["tflops"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": K,
+        "warmup": W,
         "ms_per_step": round(head["us_per_launch"] / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -275,46 +416,20 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(head["tflops"], 2),
                      "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(head["frac_of_peak"], 4), "traffic": traffic},
+        "measured_after": ("the secondary legs (GPU busy without idle gaps)" if not args.quick
+                           else "the cold-start leg"),
+        "cold_start": {"value": round(cold["tflops"], 2), "unit": "TFLOP/s",
+                       "us_per_launch": round(cold["us_per_launch"], 2),
+                       "frac": round(cold["frac_of_peak"], 4), "warmup": W, "steps": K,
+                       "note": "the first W + K launches of the process, GPU idle before: "
+                               "inside the power controller's transient"},
     }
-    if not args.quick:
-        add = stream_case(pg, inputs, args.steps, args.warmup, stream, scalar=False)
-        addc = stream_case(pg, inputs, args.steps, args.warmup, stream, scalar=True)
-        print("stream add: %.1f GB/s; x+1: %.1f GB/s" % (add["GB/s"], addc["GB/s"]),
-              file=sys.stderr, flush=True)
-        out["streaming"] = {
-            "workload": "z = x + y, fp32 8192x8192, U[-1,1], 3 rotating buffer sets",
-            "value": round(add["GB/s"], 1), "unit": "GB/s",
-            "us_per_launch": round(add["us_per_launch"], 2),
-            "roofline": {"bound": "hbm", "achieved": round(add["GB/s"], 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(add["frac_of_hbm"], 4),
-                         "traffic": measured_traffic("add_vec_kernel", src_hash)},
-            "x_plus_1": {"value": round(addc["GB/s"], 1), "unit": "GB/s",
-                         "us_per_launch": round(addc["us_per_launch"], 2),
-                         "frac": round(addc["frac_of_hbm"], 4)},
-        }
-        out["reduction"] = reduce_case(pg, inputs, max(5, args.steps // 5), max(3, args.warmup // 5),
-                                       stream)
-        print("reduction: %.1f GB/s" % out["reduction"]["value"], file=sys.stderr, flush=True)
-        others = []
-        for (M, N, K, dist) in [(8192, 8192, 8192, "normal"), (2048, 2048, 32768, "uniform"),
-                                (256, 256, 256, "uniform")]:
-            r = gemm_case(pg, inputs, M, N, K, dist, max(5, args.steps // 10), max(3, args.warmup // 10),
-                          stream)
-            print("gemm %dx%dx%d: %.1f us, %.1f TFLOP/s" % (M, N, K, r["us_per_launch"], r["tflops"]),
-                  file=sys.stderr, flush=True)
-            others.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
-        # long K through split-K (the caller provides the fp32 workspace)
-        r = gemm_case(pg, inputs, 2048, 2048, 32768, "uniform", max(5, args.steps // 10),
-                      max(3, args.warmup // 10), stream, splitk=True)
-        print("gemm 2048x2048x32768 split-K: %.1f us, %.1f TFLOP/s" % (r["us_per_launch"], r["tflops"]),
-              file=sys.stderr, flush=True)
-        others.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
-        out["other_gemm"] = others
+    out.update(out_extra)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)
-        if "streaming" in out:
-            out["streaming"]["cpu_baseline"] = cpu_baseline_stream(inputs)
+        if not args.quick:
+            out["cpu_baseline_other"] = cpu_baselines_other(inputs)
     print(json.dumps(out), flush=True)
 
 

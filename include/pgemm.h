@@ -57,7 +57,8 @@ enum pgemm_status {
  * bit-identical outputs, call after call.
  *
  * Requirements: M, N, K >= 0; K % 8 == 0 and N % 8 == 0 (rows are moved in
- * 16-byte pieces); A, B, C 16-byte aligned; K < 2^22 and N < 2^23; the C
+ * 16-byte pieces); A, B, C 16-byte aligned; K < 2^22, N < 2^23 and
+ * M*N <= 2^37 (the launch grid stays under 2^32 work-items); the C
  * range must not overlap A or B.
  *   M == 0 or N == 0: PGEMM_OK, nothing is enqueued.
  *   K == 0: C is filled with +0.0 (the empty sum).
@@ -199,7 +200,9 @@ int pstream_add(const float* x, const float* y, float* z, int64_t n,
  * elements (the block-size parameter of the guide's section 6.1, whose
  * example uses 512*512; pstream_add uses 4096, the fastest measured on
  * MI355X).  block_elems must be a positive multiple of 1024 and at most
- * 2^24, else PGEMM_EUNSUPPORTED.  Results do not depend on it.
+ * 2^24, else PGEMM_EUNSUPPORTED; so is an n of more than 2^24 - 1
+ * blocks (one launch of 256-lane workgroups stays under 2^32 work-items).
+ * Results do not depend on the block size.
  */
 int pstream_add_blocked(const float* x, const float* y, float* z, int64_t n,
                         int64_t block_elems, pgemm_stream_t stream);
@@ -209,6 +212,7 @@ int pstream_add_blocked(const float* x, const float* y, float* z, int64_t n,
  * section 4, which writes its result back over its input (z == x is
  * allowed; any other overlap returns PGEMM_EINVAL).  One binary32 addition
  * per element.  Reads one array, so it moves 8 bytes per element.
+ * n above (2^24 - 1) * 8192 is PGEMM_EUNSUPPORTED.
  */
 int pstream_add_scalar(const float* x, float c, float* z, int64_t n,
                        pgemm_stream_t stream);
@@ -223,7 +227,7 @@ int pstream_add_scalar(const float* x, float c, float* z, int64_t n,
  * plain sequential loop bit for bit.  R == 0 writes +0.0 everywhere;
  * n == 0 enqueues nothing.  o must not overlap x (PGEMM_EINVAL); null
  * pointers with non-zero sizes and negative sizes are PGEMM_EINVAL;
- * n > 2^36 or R*n > 2^40 is PGEMM_EUNSUPPORTED.  16-byte aligned x and o
+ * n >= 2^36 or R*n > 2^40 is PGEMM_EUNSUPPORTED.  16-byte aligned x and o
  * with n % 4 == 0 take the vector path.
  */
 int preduce_sum_f32(const float* x, float* o, int64_t R, int64_t n, pgemm_stream_t stream);

@@ -23,22 +23,45 @@ __all__ = [
 ]
 
 
+_TORCH = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _TORCH
+    if _TORCH is None:
+        import torch
+        _TORCH = torch
+    return _TORCH
 
 
-def _stream_handle(device, stream):
+def _raw_stream(index, stream):
+    """The hipStream_t (as an int) to launch on: `stream`'s, else the current
+    stream of device `index`."""
+    if stream is not None:
+        return stream.cuda_stream
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return s.cuda_stream
+    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if get is not None:
+        return get(index)
+    return torch.cuda.current_stream(index).cuda_stream
+
+
+def _invoke(t, stream, fn):
+    """fn(stream handle) with t's device current.  The per-call cost matters
+    for small problems, so the device is switched only when it differs."""
+    torch = _torch()
+    index = t.get_device()
+    if index == torch.cuda.current_device():
+        return fn(_raw_stream(index, stream))
+    with torch.cuda.device(index):
+        return fn(_raw_stream(index, stream))
 
 
 def _check_dev(t, dtype, name, ndim=None):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("%s must be a device (HIP) tensor, got %s" % (name, t.device))
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
@@ -63,7 +86,8 @@ def pgemm_f16_variant(A, B, variant, C=None, stream=None):
     torch = _torch()
     _check_dev(A, torch.float16, "A", 2)
     _check_dev(B, torch.float16, "B", 2)
-    if A.device != B.device:
+    dev_a = A.get_device()
+    if dev_a != B.get_device():
         raise ValueError("A and B are on different devices")
     M, K = A.shape
     K2, N = B.shape
@@ -73,11 +97,11 @@ def pgemm_f16_variant(A, B, variant, C=None, stream=None):
         C = torch.empty((M, N), dtype=torch.float16, device=A.device)
     else:
         _check_dev(C, torch.float16, "C", 2)
-        if tuple(C.shape) != (M, N) or C.device != A.device:
+        if C.shape != (M, N) or C.get_device() != dev_a:
             raise ValueError("C must be a (%d, %d) tensor on %s" % (M, N, A.device))
-    with torch.cuda.device(A.device):
-        rc = lib().pgemm_f16_variant(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K,
-                                     int(variant), _stream_handle(A.device, stream))
+    f = lib().pgemm_f16_variant
+    rc = _invoke(A, stream, lambda h: f(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K,
+                                        int(variant), h))
     _call(rc, "pgemm_f16")
     return C
 
@@ -120,11 +144,10 @@ def pgemm_f16_splitk(A, B, splits=None, C=None, workspace=None, stream=None):
         workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=A.device)
     elif workspace.device != A.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on %s" % A.device)
-    with torch.cuda.device(A.device):
-        rc = lib().pgemm_f16_splitk(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K, int(splits),
-                                    workspace.data_ptr(),
-                                    workspace.numel() * workspace.element_size(),
-                                    _stream_handle(A.device, stream))
+    f = lib().pgemm_f16_splitk
+    rc = _invoke(A, stream, lambda h: f(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K,
+                                        int(splits), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), h))
     _call(rc, "pgemm_f16_splitk")
     return C
 
@@ -159,7 +182,7 @@ def _elementwise_out(x, z):
     if z is None:
         return torch.empty_like(x)
     _check_dev(z, torch.float32, "z")
-    if z.numel() != x.numel() or z.device != x.device:
+    if z.numel() != x.numel() or z.get_device() != x.get_device():
         raise ValueError("z must have x's size and device")
     return z
 
@@ -174,16 +197,16 @@ def pstream_add_blocked(x, y, block_elems, z=None, stream=None):
     torch = _torch()
     _check_dev(x, torch.float32, "x")
     _check_dev(y, torch.float32, "y")
-    if x.numel() != y.numel() or x.device != y.device:
+    if x.numel() != y.numel() or x.get_device() != y.get_device():
         raise ValueError("x and y must have the same size and device")
     z = _elementwise_out(x, z)
-    with torch.cuda.device(x.device):
-        h = _stream_handle(x.device, stream)
-        if block_elems is None:
-            rc = lib().pstream_add(x.data_ptr(), y.data_ptr(), z.data_ptr(), x.numel(), h)
-        else:
-            rc = lib().pstream_add_blocked(x.data_ptr(), y.data_ptr(), z.data_ptr(), x.numel(),
-                                           int(block_elems), h)
+    L = lib()
+    if block_elems is None:
+        rc = _invoke(x, stream, lambda h: L.pstream_add(x.data_ptr(), y.data_ptr(), z.data_ptr(),
+                                                        x.numel(), h))
+    else:
+        rc = _invoke(x, stream, lambda h: L.pstream_add_blocked(
+            x.data_ptr(), y.data_ptr(), z.data_ptr(), x.numel(), int(block_elems), h))
     _call(rc, "pstream_add")
     return z
 
@@ -193,9 +216,8 @@ def pstream_add_scalar(x, c, z=None, stream=None):
     torch = _torch()
     _check_dev(x, torch.float32, "x")
     z = _elementwise_out(x, z)
-    with torch.cuda.device(x.device):
-        rc = lib().pstream_add_scalar(x.data_ptr(), float(c), z.data_ptr(), x.numel(),
-                                      _stream_handle(x.device, stream))
+    f = lib().pstream_add_scalar
+    rc = _invoke(x, stream, lambda h: f(x.data_ptr(), float(c), z.data_ptr(), x.numel(), h))
     _call(rc, "pstream_add_scalar")
     return z
 
@@ -214,9 +236,8 @@ def preduce_sum_f32(x, out=None, stream=None):
         _check_dev(out, torch.float32, "out")
         if tuple(out.shape) != tuple(x.shape[1:]) or out.device != x.device:
             raise ValueError("out must have shape %s on %s" % (tuple(x.shape[1:]), x.device))
-    with torch.cuda.device(x.device):
-        rc = lib().preduce_sum_f32(x.data_ptr(), out.data_ptr(), R, out.numel(),
-                                   _stream_handle(x.device, stream))
+    f = lib().preduce_sum_f32
+    rc = _invoke(x, stream, lambda h: f(x.data_ptr(), out.data_ptr(), R, out.numel(), h))
     _call(rc, "preduce_sum_f32")
     return out
 
@@ -225,9 +246,8 @@ def pgemm_test_fill_f32(n, v=42.0, device="cuda", out=None, stream=None):
     torch = _torch()
     o = out if out is not None else torch.empty(int(n), dtype=torch.float32, device=device)
     _check_dev(o, torch.float32, "out")
-    with torch.cuda.device(o.device):
-        rc = lib().pgemm_test_fill_f32(o.data_ptr(), float(v), o.numel(),
-                                       _stream_handle(o.device, stream))
+    f = lib().pgemm_test_fill_f32
+    rc = _invoke(o, stream, lambda h: f(o.data_ptr(), float(v), o.numel(), h))
     _call(rc, "pgemm_test_fill_f32")
     return o
 
@@ -236,7 +256,7 @@ def pgemm_test_iota_f32(n, device="cuda", out=None, stream=None):
     torch = _torch()
     o = out if out is not None else torch.empty(int(n), dtype=torch.float32, device=device)
     _check_dev(o, torch.float32, "out")
-    with torch.cuda.device(o.device):
-        rc = lib().pgemm_test_iota_f32(o.data_ptr(), o.numel(), _stream_handle(o.device, stream))
+    f = lib().pgemm_test_iota_f32
+    rc = _invoke(o, stream, lambda h: f(o.data_ptr(), o.numel(), h))
     _call(rc, "pgemm_test_iota_f32")
     return o

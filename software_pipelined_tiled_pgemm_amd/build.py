@@ -3,7 +3,8 @@
     python -m software_pipelined_tiled_pgemm_amd.build [--verbose]
 
 Flags: -O3; packed-fp32 instructions disabled; fp32 denormals kept (the
-streaming kernels must match IEEE binary32 bit for bit); no fast-math.
+streaming kernels must match IEEE binary32 bit for bit); no fast-math;
+explicit kernel arguments preloaded into SGPRs.
 Each source is compiled to an object (PER_FILE adds flags to single
 sources), then the objects are linked into the shared library.
 """
@@ -34,6 +35,10 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
     "-Wall",
+    # The explicit kernel arguments arrive preloaded in SGPRs instead of
+    # through a scalar load at the start of every wave (measured: 256^3 GEMM
+    # 4.94 -> 4.59 us per launch, large shapes unchanged).
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 # Extra code-generation flags of single sources.

@@ -156,7 +156,9 @@ __device__ __forceinline__ floatx4 mfma16(half8 row_op, half8 col_op, floatx4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(row_op, col_op, c, 0, 0, 0);
 }
 
-// Block id -> output tile.  Workgroups are dealt to the 8 XCDs round-robin,
+// Block id -> output tile (nwg = tiles_m * tiles_n, the grid's x extent,
+// passed from the explicit arguments so that no kernel reads a hidden
+// argument).  Workgroups are dealt to the 8 XCDs round-robin,
 // so id b runs on XCD b % 8; the first remap gives each XCD a contiguous
 // range of logical tiles.  The second walks tiles in column-major order
 // inside bands of `group_m` tile rows, so a contiguous range covers a compact
@@ -797,7 +799,7 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
     }
 
     int tm, tn;
-    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    tile_of_block(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * TL::BM, n0 = tn * TL::BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1052,7 +1054,7 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     static_assert(3 * NB + 2 * NA < 64, "vmcnt range");
 
     int tm, tn;
-    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    tile_of_block(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * TL::BM, n0 = tn * TL::BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1261,7 +1263,7 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
     __shared__ __attribute__((aligned(16))) char smem[TL::LDS];
 
     int tm, tn;
-    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    tile_of_block(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * TL::BM, n0 = tn * TL::BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;

@@ -74,6 +74,9 @@ hipError_t launch_splitk_sum(const float* W, _Float16* C, int64_t S, int64_t n,
 // one-shot blocks keep many workgroups, and so many 16-byte loads, in flight.
 constexpr int64_t kStreamDefaultBlock = 4096;
 constexpr int64_t kStreamScalarBlock = 8192;
+// Most workgroups of 256 lanes in one launch: HIP rejects a grid whose
+// dimension times the workgroup size reaches 2^32 work-items.
+constexpr int64_t kMaxGridBlocks = (((int64_t)1 << 32) - 1) / 256;
 
 hipError_t launch_stream_add(const float* x, const float* y, float* z, int64_t n,
                              int64_t block_elems, hipStream_t stream);

@@ -35,6 +35,9 @@ bool bad_alias(const void* out, const void* in, int64_t bytes) {
 constexpr int64_t kMaxK = (int64_t)1 << 22;
 constexpr int64_t kMaxN = (int64_t)1 << 23;
 constexpr int64_t kMaxM = ((int64_t)1 << 31) - 256;
+// M*N limit (256 GiB of C): keeps the tile count of a launch below 2^23, so
+// that tiles times workgroup size stays under 2^32 work-items.
+constexpr int64_t kMaxMN = (int64_t)1 << 37;
 
 int check_gemm(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return PGEMM_EINVAL;
@@ -42,7 +45,7 @@ int check_gemm(const void* A, const void* B, const void* C, int64_t M, int64_t N
     if (!C) return PGEMM_EINVAL;
     if (K > 0 && (!A || !B)) return PGEMM_EINVAL;
     if (K % 8 != 0 || N % 8 != 0) return PGEMM_EUNSUPPORTED;
-    if (K >= kMaxK || N >= kMaxN || M >= kMaxM) return PGEMM_EUNSUPPORTED;
+    if (K >= kMaxK || N >= kMaxN || M >= kMaxM || M * N > kMaxMN) return PGEMM_EUNSUPPORTED;
     if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B)))) return PGEMM_EUNSUPPORTED;
     const int64_t cb = M * N * 2;
     if (K > 0 && (overlap(C, cb, A, M * K * 2) || overlap(C, cb, B, K * N * 2)))
@@ -157,7 +160,7 @@ int pstream_add_blocked(const float* x, const float* y, float* z, int64_t n, int
     if (!x || !y || !z) return PGEMM_EINVAL;
     const int64_t bytes = n * (int64_t)sizeof(float);
     if (bad_alias(z, x, bytes) || bad_alias(z, y, bytes)) return PGEMM_EINVAL;
-    if ((n + block_elems - 1) / block_elems > 0x7FFFFFFF) return PGEMM_EUNSUPPORTED;
+    if ((n + block_elems - 1) / block_elems > pgemm::kMaxGridBlocks) return PGEMM_EUNSUPPORTED;
     return hip_status(
         pgemm::launch_stream_add(x, y, z, n, block_elems, static_cast<hipStream_t>(stream)));
 }
@@ -171,6 +174,8 @@ int pstream_add_scalar(const float* x, float c, float* z, int64_t n, pgemm_strea
     if (n == 0) return PGEMM_OK;
     if (!x || !z) return PGEMM_EINVAL;
     if (bad_alias(z, x, n * (int64_t)sizeof(float))) return PGEMM_EINVAL;
+    if ((n + pgemm::kStreamScalarBlock - 1) / pgemm::kStreamScalarBlock > pgemm::kMaxGridBlocks)
+        return PGEMM_EUNSUPPORTED;
     return hip_status(pgemm::launch_stream_add_scalar(x, c, z, n, static_cast<hipStream_t>(stream)));
 }
 
@@ -178,7 +183,8 @@ int preduce_sum_f32(const float* x, float* o, int64_t R, int64_t n, pgemm_stream
     if (R < 0 || n < 0) return PGEMM_EINVAL;
     if (n == 0) return PGEMM_OK;
     if (!o || (R > 0 && !x)) return PGEMM_EINVAL;
-    if (n > ((int64_t)1 << 36) || R > ((int64_t)1 << 40) / n) return PGEMM_EUNSUPPORTED;
+    // n < 2^36: at most 2^24 - 1 workgroups of 4096 outputs.
+    if (n >= ((int64_t)1 << 36) || R > ((int64_t)1 << 40) / n) return PGEMM_EUNSUPPORTED;
     if (R > 0 && overlap(o, n * 4, x, R * n * 4)) return PGEMM_EINVAL;
     return hip_status(pgemm::launch_sum_axis0(R > 0 ? x : o, o, R, n,
                                               static_cast<hipStream_t>(stream)));

@@ -69,27 +69,28 @@ __global__ __launch_bounds__(kThreads) void sum_axis0_vec_kernel(const float* x,
             __builtin_nontemporal_store(acc[u], reinterpret_cast<floatx4*>(o) + base + u * kThreads);
 }
 
-// Any alignment or length: one output element per lane.
+// Any alignment or length: one output element per lane and iteration of a
+// grid-stride loop (the grid is capped, n is not).
 __global__ __launch_bounds__(kThreads) void sum_axis0_scalar_kernel(const float* x, float* o,
                                                                     int64_t R, int64_t n) {
-    const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (j >= n) return;
-    float acc = 0.0f;
-    for (int64_t i = 0; i < R; ++i) acc = acc + x[i * n + j];
-    o[j] = acc;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < n; j += stride) {
+        float acc = 0.0f;
+        for (int64_t i = 0; i < R; ++i) acc = acc + x[i * n + j];
+        o[j] = acc;
+    }
 }
 
 // Split-K finish: C[i] = fp16_rne(W[0][i] + W[1][i] + ... + W[S-1][i]), the
 // partials added in ascending order from +0.0f in fp32.  Lane t owns 8
 // consecutive outputs (two float4 per partial, one 16-byte fp16 store); n is
 // a multiple of 8 and both arrays are 16-byte aligned.
-__global__ __launch_bounds__(kThreads) void splitk_sum_kernel(const float* W, _Float16* C,
-                                                              int64_t S, int64_t n) {
+// Group j of the split-K finish (outputs 8j .. 8j+7).
+__device__ __forceinline__ void splitk_sum_group(const float* W, _Float16* C, int64_t S, int64_t n,
+                                                 int64_t j) {
     typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
     typedef float float2_t __attribute__((ext_vector_type(2)));
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // group of 8
-    if (8 * j >= n) return;
     const floatx4* src = reinterpret_cast<const floatx4*>(W) + 2 * j;
     const int64_t stride = n / 4;  // one partial, in float4
     floatx4 lo = {0.0f, 0.0f, 0.0f, 0.0f}, hi = lo;
@@ -114,13 +115,24 @@ __global__ __launch_bounds__(kThreads) void splitk_sum_kernel(const float* W, _F
     __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(C) + j);
 }
 
+// The grid is capped (kMaxGridBlocks), so a lane walks groups j, j + lanes of
+// the grid, ...
+__global__ __launch_bounds__(kThreads) void splitk_sum_kernel(const float* W, _Float16* C,
+                                                              int64_t S, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; 8 * j < n; j += stride)
+        splitk_sum_group(W, C, S, n, j);
+}
+
 }  // namespace
 
 hipError_t launch_splitk_sum(const float* W, _Float16* C, int64_t S, int64_t n,
                              hipStream_t stream) {
     const int64_t groups = n / 8;
-    hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)((groups + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, W, C, S, n);
+    int64_t blocks = (groups + kThreads - 1) / kThreads;
+    if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
+    hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, W, C,
+                       S, n);
     return hipGetLastError();
 }
 
@@ -133,8 +145,10 @@ hipError_t launch_sum_axis0(const float* x, float* o, int64_t R, int64_t n, hipS
         hipLaunchKernelGGL(sum_axis0_vec_kernel, dim3((unsigned)((lanes + per_block - 1) / per_block)),
                            dim3(kThreads), 0, stream, x, o, R, n);
     } else {
-        hipLaunchKernelGGL(sum_axis0_scalar_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, stream, x, o, R, n);
+        int64_t blocks = (n + kThreads - 1) / kThreads;
+        if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
+        hipLaunchKernelGGL(sum_axis0_scalar_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, x, o, R, n);
     }
     return hipGetLastError();
 }

@@ -63,6 +63,7 @@ A, B, C = 0x10000000, 0x20000000, 0x30000000
     ((A, B + 8, C, 8, 8, 8), EUNSUP),
     ((A, B, C + 4, 8, 8, 8), EUNSUP),
     ((A, B, C, 8, 8, 1 << 22), EUNSUP),     # K limit
+    ((A, B, C, (1 << 30) + 256, 1 << 7, 8), EUNSUP),  # M*N above 2^37: grid limit
     ((A, B, A + 16, 8, 8, 8), EINVAL),      # C overlaps A
     ((A, B, B, 8, 8, 8), EINVAL),           # C is B
     ((0, 0, 0, 0, 8, 8), OK),               # empty: nothing enqueued
@@ -133,6 +134,10 @@ def test_stream_add_block_checks(L):
     assert L.pstream_add_blocked(A, B, C, 16, 1000, None) == EUNSUP
     assert L.pstream_add_blocked(A, B, C, 16, (1 << 24) + 1024, None) == EUNSUP
     assert L.pstream_add_blocked(A, B, C, 0, 1024, None) == OK
+    # 2^24 blocks of 256 lanes would reach 2^32 work-items in one launch
+    X, Y, Z = 1 << 44, 2 << 44, 3 << 44  # far enough apart for these sizes
+    assert L.pstream_add_blocked(X, Y, Z, 1024 << 24, 1024, None) == EUNSUP
+    assert L.pstream_add_scalar(X, 1.0, Z, (8192 << 24) - 8191, None) == EUNSUP
 
 
 def test_scalar_and_test_kernels_argument_checks(L):
@@ -154,6 +159,7 @@ def test_reduce_argument_checks(L):
     assert L.preduce_sum_f32(A, A + 64, 8, 8, None) == EINVAL      # o inside x
     assert L.preduce_sum_f32(A, C, 8, 0, None) == OK                # nothing to do
     assert L.preduce_sum_f32(A, C, 1 << 30, 1 << 20, None) == EUNSUP
+    assert L.preduce_sum_f32(A, C, 1, 1 << 36, None) == EUNSUP     # 2^24 workgroups of 4096
 
 
 def test_python_binding_rejects_cpu_tensors():

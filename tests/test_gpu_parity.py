@@ -6,8 +6,9 @@ Bars: bit-exact for the streaming add, x + c, fill and iota; for the GEMM
 bit-exact where the exact result is an fp16 value that fp32 accumulation
 reaches exactly (identity, ones, power-of-two rank-1).  Full-size GEMMs are
 checked on a deterministic sample of outputs computed one by one by the
-oracle; smaller shapes that span several tiles and a ragged edge are checked
-element by element."""
+oracle (the headline 4096^3 configuration also on every output); smaller
+shapes that span several tiles and a ragged edge are checked element by
+element."""
 import sys
 
 import numpy as np
@@ -100,6 +101,18 @@ def test_iota_matches_pages():
 def test_iota_large_vs_oracle(n):
     say("iota n=%d" % n)
     assert bits_equal(host(pg.pgemm_test_iota_f32(n)), oracle.iota_f32(n))
+
+
+def test_iota_past_2_31_elements():
+    """More elements than 2^31: the launch widens each workgroup's slice so
+    that the grid stays under 2^32 work-items (with 128 elements per
+    workgroup it would not launch)."""
+    n = (1 << 31) + 5
+    say("iota n=%d" % n)
+    o = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    got = host(pg.pgemm_test_iota_f32(n, out=o))
+    del o
+    assert bits_equal(got, oracle.iota_f32(n))
 
 
 def test_ones_add_512_matches_pages():
@@ -458,6 +471,26 @@ def test_gemm_full_size_sampled(name, M, N, K, dist):
     say("  relative Frobenius error against the exact sums: %.3e" % (np.linalg.norm(g - S) / np.linalg.norm(S)))
     _, Sabs = oracle.gemm_f16_points(np.abs(A), np.abs(B), I, J)
     assert_fp32_bound(got[I, J], ref, Sabs, K, name)
+
+
+def test_gemm_4096_every_output_vs_oracle():
+    """The headline configuration (4096^3, U[-1,1]) on every one of its
+    16,777,216 outputs: the whole result against the oracle, as the
+    quickstart's matmul example checks its whole result against a @ b.
+    Automatic variant (what the benchmark times), C poisoned with NaN first."""
+    M = N = K = 4096
+    say("gemm 4096^3 uniform, every output against the oracle (%d oracle threads)" % oracle.threads())
+    A, B = inputs.gemm_inputs(M, N, K, "uniform")
+    C = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda:0")
+    got = gemm(A, B, C=C)
+    assert not np.isnan(got).any(), "NaN left in C"
+    ref, S = oracle.gemm_f16(A, B)
+    assert_close(got, ref, "4096^3 every output")
+    d = np.abs(got.view(np.uint16).astype(np.int64) - ref.view(np.uint16).astype(np.int64))
+    say("  max |ulp diff| %d, frac exact %.4f, relative Frobenius error against the exact sums %.3e"
+        % (d.max(), np.mean(d == 0), np.linalg.norm(got.astype(np.float64) - S) / np.linalg.norm(S)))
+    _, Sabs = oracle.gemm_f16(np.abs(A), np.abs(B))
+    assert_fp32_bound(got, ref, Sabs, K, "4096^3 every output")
 
 
 # ------------------------------------------------------------ automatic row split
