@@ -68,8 +68,9 @@ def parse():
 def profile_run(pg, inputs, reps):
     """Launch sequence for counter collection: one plain copy of known size
     (512 MiB read + 512 MiB written) to calibrate FETCH_SIZE / WRITE_SIZE,
-    then `reps` launches each of the 4096^3 GEMM, the streaming add, x + 1
-    and the (8, 4096, 4096) reduction."""
+    then `reps` launches each of the 4096^3 GEMM, the streaming add, x + 1,
+    the (8, 4096, 4096) reduction, the 8192^3 GEMM, the 2048^2 x 32768 GEMM
+    and its split-K form."""
     import torch
     src = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -93,6 +94,13 @@ def profile_run(pg, inputs, reps):
     o = torch.empty((4096, 4096), dtype=torch.float32, device="cuda")
     for _ in range(reps):
         pg.preduce_sum_f32(xr, out=o)
+    del xr, o
+    for (M, N, K, dist) in [(8192, 8192, 8192, "normal"), (2048, 2048, 32768, "uniform")]:
+        tA, tB, tC = gemm_operands(inputs, M, N, K, dist)
+        for _ in range(reps):
+            pg.pgemm_f16(tA, tB, C=tC)
+    for _ in range(reps):
+        pg.pgemm_f16_splitk(tA, tB, C=tC)
     torch.cuda.synchronize()
     print("profile launches done", flush=True)
 

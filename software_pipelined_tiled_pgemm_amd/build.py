@@ -1,6 +1,6 @@
 """Builds libpgemm.so (gfx950) in-tree with hipcc.
 
-    python -m software_pipelined_tiled_pgemm_amd.build [--verbose]
+    python -m software_pipelined_tiled_pgemm_amd.build [--verbose] [--poison-lds]
 
 Flags: -O3; packed-fp32 instructions disabled; fp32 denormals kept (the
 streaming kernels must match IEEE binary32 bit for bit); no fast-math;
@@ -91,5 +91,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose="--verbose" in sys.argv)
+    # --poison-lds: the race-detection build (released LDS stages filled with
+    # NaN behind an extra barrier); for test runs only, never the product.
+    build(verbose="--verbose" in sys.argv,
+          extra_flags=["-DPGEMM_POISON_LDS=1"] if "--poison-lds" in sys.argv else None)
     print(LIB)

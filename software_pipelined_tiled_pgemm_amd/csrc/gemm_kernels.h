@@ -132,6 +132,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const LDS_AS char*)p;
 }
 
+// Race-detection build (PGEMM_POISON_LDS=1, never the product): right after
+// the barrier that releases a ring stage, the workgroup fills it with fp16
+// NaN and passes one more barrier before any copy may refill it.  A read of
+// the stage after its release -- the overwrite the quickstart's
+// delay_release guards against -- then yields NaN in C instead of a silently
+// wrong value.  `threads` lanes (all of the workgroup's) share the writes.
+#ifndef PGEMM_POISON_LDS
+#define PGEMM_POISON_LDS 0
+#endif
+template <int BYTES, int THREADS>
+__device__ __forceinline__ void poison_stage(char* stage, int tid) {
+    const u32x4 nan4 = {0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u};
+    for (int o = tid * 16; o < BYTES; o += THREADS * 16)
+        *reinterpret_cast<u32x4*>(stage + o) = nan4;
+}
+
 // s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left at their "no wait" maxima),
 // gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14.
 template <int N>
@@ -891,6 +907,10 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
             // copy_wait for step kt+1; the barrier also releases slot se
             wait_vmcnt<5 * H>();
             __syncthreads();
+            if constexpr (PGEMM_POISON_LDS) {
+                poison_stage<TL::STAGE, TL::T>(smem + se * TL::STAGE, tid);
+                __syncthreads();
+            }
             // second half of step kt (reads of step kt+1 begin); first A pairs
             cm.template half<1, H>(nxt, wm, wn, lane,
                                    [&](int q) __attribute__((always_inline)) { pairs(q, 0); });
@@ -901,6 +921,10 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
             // copy_wait for step kt+2; the barrier also releases slot s1
             wait_vmcnt<4 * H>();
             __syncthreads();
+            if constexpr (PGEMM_POISON_LDS) {
+                poison_stage<TL::STAGE, TL::T>(smem + s1 * TL::STAGE, tid);
+                __syncthreads();
+            }
             // second half of step kt+1 (reads of step kt+2 begin); B of step kt+5
             cm.template half<3, H>(smem + s2 * TL::STAGE, wm, wn, lane,
                                    [&](int q) __attribute__((always_inline)) {
@@ -1081,9 +1105,11 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
                 pr.b_step(B, N, K, n0, kt + 4, ring + s4 * TL::STAGE);
                 wait_vmcnt<3 * NB + 2 * NA>();  // step kt+1 landed
                 __syncthreads();
+                if constexpr (PGEMM_POISON_LDS) __syncthreads();  // MFMA waves poison slot se
                 pr.a_pairs(A, M, K, m0, kt + 4, ring + s4 * TL::STAGE, ring + se * TL::STAGE);
                 wait_vmcnt<2 * NB + 2 * NA>();  // step kt+2 landed
                 __syncthreads();
+                if constexpr (PGEMM_POISON_LDS) __syncthreads();  // MFMA waves poison slot s1
                 se = s2;
             }
             wait_vmcnt<0>();  // the copies past the end of K
@@ -1114,9 +1140,17 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
             const char* nxt = smem + s1 * TL::STAGE;
             dm::half_step<TL, 0>(acc, fa[0], fb[0], cur, 1, fa[1], fb[1], wm, wn, lane, none);
             __syncthreads();  // step kt+1 landed; slot se released
+            if constexpr (PGEMM_POISON_LDS) {
+                poison_stage<TL::STAGE, TL::T>(smem + se * TL::STAGE, tid);
+                __syncthreads();
+            }
             dm::half_step<TL, 0>(acc, fa[1], fb[1], nxt, 0, fa[0], fb[0], wm, wn, lane, none);
             dm::half_step<TL, 0>(acc, fa[0], fb[0], nxt, 1, fa[1], fb[1], wm, wn, lane, none);
             __syncthreads();  // step kt+2 landed; slot s1 released
+            if constexpr (PGEMM_POISON_LDS) {
+                poison_stage<TL::STAGE, TL::T>(smem + s1 * TL::STAGE, tid);
+                __syncthreads();
+            }
             dm::half_step<TL, 0>(acc, fa[1], fb[1], smem + s2 * TL::STAGE, 0, fa[0], fb[0], wm, wn,
                                  lane, none);
             se = s2;
@@ -1301,6 +1335,10 @@ void kernel(const _Float16* __restrict__ A, const _Float16* __restrict__ B,
                     read_frags<TL>(cur, s + 1, wm, wn, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
                 } else {
                     __syncthreads();  // publishes `nxt`, releases `cur`
+                    if constexpr (PGEMM_POISON_LDS) {
+                        poison_stage<TL::STAGE, TL::T>(cur, tid);
+                        __syncthreads();
+                    }
                     if (kt + 1 < nk) read_frags<TL>(nxt, 0, wm, wn, lane, fa[0], fb[0]);
                 }
                 mfma_block<TL>(acc, fa[s & 1], fb[s & 1]);

@@ -49,17 +49,8 @@ struct AddSlot {
 // One workgroup per block of `block` elements (block is a multiple of 1024,
 // so a block starts 16-byte aligned whenever the arrays do).  Group g of a
 // block is float4s g*kUnroll*kThreads .. +kUnroll*kThreads-1, lane t taking
-// every kThreads-th.  A workgroup walks its block's groups starting at group
-// (b * kWalkStride) mod groups and wrapping around, so that workgroups whose
-// blocks lie a power-of-two distance apart do not read and write the same
-// offsets of their blocks at the same time.  The last block may be ragged:
-// its whole float4s past the last full group and its scalar tail are
-// handled by the same workgroup.
-#ifndef PGEMM_WALK_STRIDE
-#define PGEMM_WALK_STRIDE 0
-#endif
-constexpr int64_t kWalkStride = PGEMM_WALK_STRIDE;
-
+// every kThreads-th.  The last block may be ragged: its whole float4s past
+// the last full group and its scalar tail are handled by the same workgroup.
 __global__ __launch_bounds__(kThreads) void add_vec_kernel(const float* x, const float* y,
                                                            float* z, int64_t n, int64_t block) {
     const int64_t start = (int64_t)blockIdx.x * block;
@@ -70,27 +61,20 @@ __global__ __launch_bounds__(kThreads) void add_vec_kernel(const float* x, const
     floatx4* zv = reinterpret_cast<floatx4*>(z + start);
     constexpr int64_t G = (int64_t)kUnroll * kThreads;
     const int64_t groups = nv / G;
-    const int64_t rot = groups > 1 ? ((int64_t)blockIdx.x * kWalkStride) % groups : 0;
     const int t = threadIdx.x;
-    auto at = [&](int64_t g) {  // float4 offset of walk step g
-        const int64_t r = g + rot;
-        return (r < groups ? r : r - groups) * G + t;
-    };
     ring_pipeline<kStages, AddSlot>(
         groups,
         [&](int64_t g, AddSlot& sl) {
-            const int64_t o = at(g);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                sl.a[u] = __builtin_nontemporal_load(xv + o + u * kThreads);
-                sl.b[u] = __builtin_nontemporal_load(yv + o + u * kThreads);
+                sl.a[u] = __builtin_nontemporal_load(xv + g * G + u * kThreads + t);
+                sl.b[u] = __builtin_nontemporal_load(yv + g * G + u * kThreads + t);
             }
         },
         [&](int64_t g, const AddSlot& sl) {
-            const int64_t o = at(g);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
-                __builtin_nontemporal_store(sl.a[u] + sl.b[u], zv + o + u * kThreads);
+                __builtin_nontemporal_store(sl.a[u] + sl.b[u], zv + g * G + u * kThreads + t);
         });
     for (int64_t i = groups * G + t; i < nv; i += kThreads) zv[i] = xv[i] + yv[i];
     for (int64_t e = (nv << 2) + t; e < len; e += kThreads) z[start + e] = x[start + e] + y[start + e];
