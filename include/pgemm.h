@@ -37,7 +37,8 @@ enum pgemm_status {
     PGEMM_OK = 0,
     PGEMM_EINVAL = -1,       /* null pointer with a non-zero size, negative size, overlap */
     PGEMM_EUNSUPPORTED = -2, /* valid request outside what the kernels handle */
-    PGEMM_EHIP = -3          /* the HIP launch failed */
+    PGEMM_EHIP = -3,         /* the HIP launch failed */
+    PGEMM_ESCRATCH = -4      /* needs more than the static scratch buffer holds */
 };
 
 /*
@@ -130,6 +131,27 @@ int pgemm_f16_splitk(const void* A, const void* B, void* C,
                      int64_t M, int64_t N, int64_t K, int splits,
                      void* workspace, int64_t workspace_bytes,
                      pgemm_stream_t stream);
+
+/*
+ * pgemm_f16_splitk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The fp32 partials go to a static
+ * device buffer of PGEMM_STATIC_SCRATCH_BYTES that the library's code object
+ * holds on every device it is loaded on, until the process ends; the call
+ * itself allocates nothing (no hipMalloc, no allocating library routine).
+ * Results are bit-identical to pgemm_f16_splitk with the same arguments.
+ * The buffer is one per device and shared by every call on it: calls that
+ * overlap in time on one device (concurrent streams, or several host
+ * threads) race on it and must be serialised by the caller.  No part of it
+ * needs to start at zero: each call writes every partial it reads.
+ * Returns PGEMM_ESCRATCH when pgemm_f16_splitk_workspace_bytes(M, N, K,
+ * splits) exceeds PGEMM_STATIC_SCRATCH_BYTES (nothing is enqueued), else as
+ * pgemm_f16_splitk.
+ */
+#define PGEMM_STATIC_SCRATCH_BYTES ((int64_t)64 << 20)
+int pgemm_f16_splitk_noalloc(const void* A, const void* B, void* C,
+                             int64_t M, int64_t N, int64_t K, int splits,
+                             pgemm_stream_t stream);
 
 /* Workspace bytes pgemm_f16_splitk needs (0 when K forms a single chunk);
  * PGEMM_EINVAL / PGEMM_EUNSUPPORTED (negative) on invalid arguments. */

@@ -9,17 +9,19 @@ missing library raises -- there is no CPU fallback.
 """
 from __future__ import annotations
 
-from ._lib import (PGEMM_EHIP, PGEMM_EINVAL, PGEMM_EUNSUPPORTED, PGEMM_OK, PgemmError,
-                   lib, status_string)
+from ._lib import (PGEMM_EHIP, PGEMM_EINVAL, PGEMM_ESCRATCH, PGEMM_EUNSUPPORTED, PGEMM_OK,
+                   STATIC_SCRATCH_BYTES, PgemmError, lib, status_string)
 
 __all__ = [
     "pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants", "pgemm_f16_choose_variant",
     "pgemm_f16_plan",
-    "pgemm_f16_splitk", "pgemm_f16_splitk_workspace_bytes", "pgemm_f16_splitk_default_splits",
+    "pgemm_f16_splitk", "pgemm_f16_splitk_noalloc", "pgemm_f16_splitk_workspace_bytes",
+    "pgemm_f16_splitk_default_splits",
     "pstream_add", "pstream_add_blocked", "pstream_add_scalar", "preduce_sum_f32",
     "pgemm_test_fill_f32", "pgemm_test_iota_f32",
     "lib", "status_string", "PgemmError",
-    "PGEMM_OK", "PGEMM_EINVAL", "PGEMM_EUNSUPPORTED", "PGEMM_EHIP",
+    "PGEMM_OK", "PGEMM_EINVAL", "PGEMM_EUNSUPPORTED", "PGEMM_EHIP", "PGEMM_ESCRATCH",
+    "STATIC_SCRATCH_BYTES",
 ]
 
 
@@ -149,6 +151,33 @@ def pgemm_f16_splitk(A, B, splits=None, C=None, workspace=None, stream=None):
                                         int(splits), workspace.data_ptr(),
                                         workspace.numel() * workspace.element_size(), h))
     _call(rc, "pgemm_f16_splitk")
+    return C
+
+
+def pgemm_f16_splitk_noalloc(A, B, splits=None, C=None, stream=None):
+    """pgemm_f16_splitk with the partials in the library's static device
+    buffer (no workspace, no allocation by the library; C is allocated here
+    only when not given).  Calls that overlap on one device race on that
+    buffer."""
+    torch = _torch()
+    _check_dev(A, torch.float16, "A", 2)
+    _check_dev(B, torch.float16, "B", 2)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2 or A.get_device() != B.get_device():
+        raise ValueError("inner dimensions or devices differ")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    else:
+        _check_dev(C, torch.float16, "C", 2)
+        if C.shape != (M, N) or C.get_device() != A.get_device():
+            raise ValueError("C must be a (%d, %d) tensor on %s" % (M, N, A.device))
+    if splits is None:
+        splits = pgemm_f16_splitk_default_splits(M, N, K)
+    f = lib().pgemm_f16_splitk_noalloc
+    rc = _invoke(A, stream, lambda h: f(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K,
+                                        int(splits), h))
+    _call(rc, "pgemm_f16_splitk_noalloc")
     return C
 
 

@@ -18,6 +18,8 @@ PGEMM_OK = 0
 PGEMM_EINVAL = -1
 PGEMM_EUNSUPPORTED = -2
 PGEMM_EHIP = -3
+PGEMM_ESCRATCH = -4
+STATIC_SCRATCH_BYTES = 64 << 20  # PGEMM_STATIC_SCRATCH_BYTES of include/pgemm.h
 
 _lib = None
 
@@ -37,6 +39,7 @@ def _declare(lib):
         "pgemm_f16_choose_variant": (i32, [i64, i64, i64]),
         "pgemm_f16_plan": (i32, [i64, i64, i64, i32, p, p, p]),
         "pgemm_f16_splitk": (i32, [p, p, p, i64, i64, i64, i32, p, i64, p]),
+        "pgemm_f16_splitk_noalloc": (i32, [p, p, p, i64, i64, i64, i32, p]),
         "pgemm_f16_splitk_workspace_bytes": (i64, [i64, i64, i64, i32]),
         "pgemm_f16_splitk_default_splits": (i32, [i64, i64, i64]),
         "pstream_add": (i32, [p, p, p, i64, p]),

@@ -68,6 +68,10 @@ hipError_t launch_gemm_f16_splitk(const void* A, const void* B, void* C, int64_t
                                   hipStream_t stream);
 hipError_t launch_splitk_sum(const float* W, _Float16* C, int64_t S, int64_t n,
                              hipStream_t stream);
+// Device address of the current device's copy of the static split-K scratch
+// buffer (PGEMM_STATIC_SCRATCH_BYTES), looked up once per device
+// (splitk_static.hip).
+hipError_t static_scratch(float** out);
 
 // Elements per workgroup block of the streaming kernels (the block-size knob
 // of the pipelined elementwise add), chosen by measurement on MI355X: small

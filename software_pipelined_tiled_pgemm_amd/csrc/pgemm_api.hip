@@ -134,6 +134,26 @@ int pgemm_f16_splitk(const void* A, const void* B, void* C, int64_t M, int64_t N
         static_cast<hipStream_t>(stream)));
 }
 
+int pgemm_f16_splitk_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                             int64_t K, int splits, pgemm_stream_t stream) {
+    if (splits < 1 || splits > kMaxSplits) return PGEMM_EUNSUPPORTED;
+    const int rc = check_gemm(A, B, C, M, N, K);
+    if (rc != PGEMM_OK) return rc;
+    if (M == 0 || N == 0) return PGEMM_OK;
+    const int64_t parts = splitk_parts(K, splits);
+    if (parts <= 1)  // one chunk: exactly pgemm_f16, no partials
+        return hip_status(pgemm::launch_gemm_f16(A, B, C, M, N, K, pgemm::kGemmAuto,
+                                                 static_cast<hipStream_t>(stream)));
+    if (M * N > kMaxSplitElems) return PGEMM_EUNSUPPORTED;
+    if (parts * M * N * 4 > PGEMM_STATIC_SCRATCH_BYTES) return PGEMM_ESCRATCH;
+    float* W = nullptr;
+    const hipError_t e = pgemm::static_scratch(&W);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(pgemm::launch_gemm_f16_splitk(A, B, C, M, N, K, splitk_chunk(K, splits),
+                                                    (int)parts, W,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 int pgemm_f16_choose_variant(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return PGEMM_EINVAL;
     return pgemm::gemm_choose_variant(M, N, K);
@@ -210,6 +230,9 @@ const char* pgemm_status_string(int status) {
         case PGEMM_EINVAL: return "invalid argument (null pointer, negative size or overlapping buffers)";
         case PGEMM_EUNSUPPORTED: return "unsupported request (alignment, divisibility, size limit or variant)";
         case PGEMM_EHIP: return "HIP kernel launch failed";
+        case PGEMM_ESCRATCH:
+            return "split-K partials exceed the static scratch buffer (PGEMM_STATIC_SCRATCH_BYTES); "
+                   "pgemm_f16_splitk takes a caller workspace of any size";
         default: return "unknown status";
     }
 }

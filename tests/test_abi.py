@@ -23,6 +23,7 @@ def L():
 def test_header_declares_the_boundary():
     names = _lib.declared_functions()
     for n in ["pgemm_f16", "pgemm_f16_variant", "pgemm_f16_num_variants", "pgemm_f16_splitk",
+              "pgemm_f16_splitk_noalloc",
               "pgemm_f16_splitk_workspace_bytes", "pgemm_f16_choose_variant", "pgemm_f16_plan",
               "pstream_add",
               "pstream_add_blocked", "pstream_add_scalar", "pgemm_test_fill_f32",
@@ -38,7 +39,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for s in (0, -1, -2, -3, 7):
+    for s in (0, -1, -2, -3, -4, 7):
         assert isinstance(pg.status_string(s), str) and pg.status_string(s)
     assert pg.status_string(0) == "ok"
     assert L.pgemm_last_hip_error() == 0
@@ -98,6 +99,17 @@ def test_splitk_workspace_bytes(L):
 ])
 def test_splitk_argument_checks(L, args, expected):
     assert L.pgemm_f16_splitk(*args, None) == expected
+
+
+@pytest.mark.parametrize("args,expected", [
+    ((A, B, C, 2048, 2048, 40960, 5), pg.PGEMM_ESCRATCH),   # 80 MiB of partials
+    ((A, B, C, 64, 64, 512, 0), EUNSUP),                   # splits out of range
+    ((A, B, C, 64, 12, 512, 4), EUNSUP),                   # N % 8
+    ((A, B, A + 16, 64, 64, 512, 4), EINVAL),              # C overlaps A
+    ((0, 0, 0, 0, 64, 512, 4), OK),                        # empty: nothing enqueued
+])
+def test_splitk_noalloc_argument_checks(L, args, expected):
+    assert L.pgemm_f16_splitk_noalloc(*args, None) == expected
 
 
 def test_splitk_default_splits(L):
