@@ -62,6 +62,9 @@ def parse():
                          "launches of each kernel, for rocprofv3 runs")
     ap.add_argument("--profile-reps", type=int, default=3,
                     help="launches of each kernel in --profile mode")
+    ap.add_argument("--fixed-cost", action="store_true",
+                    help="also time the 256x256-tile GEMM at M=N=4096 for K = 0 .. 4096 and fit "
+                         "time = fixed + steps * per_step (the per-launch cost outside the K loop)")
     return ap.parse_args()
 
 
@@ -225,6 +228,35 @@ def reduce_case(pg, sets, out, steps, warmup, stream, settle_s):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic("sum_axis0_vec_kernel", kernel_source_hash())}}
+
+
+def fixed_cost(pg, inputs, stream, settle_s):
+    """Per-launch time of the 4096^3 headline kernel (variant 8) at M=N=4096
+    for several K, and a least-squares line time = fixed + steps * per_step
+    over K >= 512 (steps = K / 32).  K = 0 runs the launch and the drain of
+    a zero tile only."""
+    import torch
+    M = N = 4096
+    A, B = inputs.gemm_inputs(M, N, 4096)
+    tA, tB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    tC = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    pts = []
+    for K in (0, 256, 512, 1024, 2048, 4096):
+        a = tA[:, :K].contiguous() if K < 4096 else tA
+        b = tB[:K].contiguous()
+        fn = lambda i: pg.pgemm_f16_variant(a, b, 8, C=tC)
+        reps = 400 if K <= 1024 else 200
+        secs, _ = time_launches(fn, reps, 20, stream, settle_s)
+        pts.append((K, secs / reps * 1e6))
+    fit = [(K // 32, t) for K, t in pts if K >= 512]
+    n = len(fit)
+    sx = sum(x for x, _ in fit); sy = sum(y for _, y in fit)
+    sxx = sum(x * x for x, _ in fit); sxy = sum(x * y for x, y in fit)
+    slope = (n * sxy - sx * sy) / (n * sxx - sx * sx)
+    icpt = (sy - slope * sx) / n
+    return {"workload": "pgemm_f16_variant 8, M=N=4096, K from 0 to 4096",
+            "us_per_launch": {str(K): round(t, 2) for K, t in pts},
+            "fit_K_ge_512": {"fixed_us": round(icpt, 2), "us_per_K_step_of_32": round(slope, 4)}}
 
 
 # ------------------------------------------------------------------ CPU baselines
@@ -433,6 +465,9 @@ def main():
                                "inside the power controller's transient"},
     }
     out.update(out_extra)
+    if args.fixed_cost:
+        out["fixed_cost"] = fixed_cost(pg, inputs, stream, settle_s)
+        print("fixed cost: %s" % out["fixed_cost"]["fit_K_ge_512"], file=sys.stderr, flush=True)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)
