@@ -141,6 +141,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 #ifndef PGEMM_POISON_LDS
 #define PGEMM_POISON_LDS 0
 #endif
+
 template <int BYTES, int THREADS>
 __device__ __forceinline__ void poison_stage(char* stage, int tid) {
     const u32x4 nan4 = {0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u};
@@ -651,6 +652,20 @@ __device__ __forceinline__ half8 read_b16(const char* stage, int j, int wn, int 
     return __builtin_bit_cast(half8, u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
 
+// MFMA slot (of NS) after which copy c (of NC) of a 16x16x32 half-step is
+// issued.  256x256 tile: spread evenly, copy c after slot (2c+1)NS/(2NC).
+// 128x128 tile (one MFMA wave per SIMD, 8 slots per half): the copies go
+// into the second-to-last slots (5 and 6), after the half's operand reads.
+// Measured on MI355X against the even spread: 2048^2 x 32768 +2.3%,
+// 1024 x 8192 x 4096 +1.2%, 512 x 4096 x 4096 +1.1%, 2048^3 -0.4%.  For the
+// 256x256 tile the spread (slots 4 and 12) is best: offsets 3 and 5 tie,
+// 6 loses 0.6%, and 0, 2 or 7 (copies among the half's first reads or right
+// before the barrier) lose 8-12%.
+template <class TL>
+__device__ __forceinline__ constexpr int copy_slot(int c, int nc, int ns) {
+    return TL::BM == 128 ? ns - 1 - nc + c : (2 * c + 1) * ns / (2 * (nc > 0 ? nc : 1));
+}
+
 // One half of a K step on the 16x16x32 path.  A step's FM16 x FN16 MFMAs
 // (all of the stage's K 32) are split by B block: half 0 takes blocks
 // j < FN16/2, half 1 the others; inside a half, j-major with i snaking, so
@@ -664,8 +679,8 @@ __device__ __forceinline__ half8 read_b16(const char* stage, int j, int wn, int 
 // So every read of a stage is issued between the barrier that publishes it
 // (the one in the middle of the previous step) and the one in the middle of
 // its own step, which releases the slot -- the same rule as the 32x32x16
-// path.  Reads take the first slots in consumption order; NC copies are
-// spread evenly over the MFMA slots.
+// path.  Reads take the first slots in consumption order; the NC copies go
+// after the slots copy_slot gives.
 template <class TL, int HALF, int NC, class CopyFn>
 __device__ __forceinline__ void half16(floatx4 (&acc)[TL::FN16][TL::FM16],
                                        const half8 (&fa)[TL::FM16], half8 (&fb)[TL::FN16],
@@ -674,7 +689,6 @@ __device__ __forceinline__ void half16(floatx4 (&acc)[TL::FN16][TL::FM16],
     constexpr int FM = TL::FM16, JH = TL::FN16 / 2;
     constexpr int NS = JH * FM;                      // MFMA slots
     constexpr int NR = HALF == 0 ? JH : FM + JH;     // read units
-    constexpr int ND = NC > 0 ? NC : 1;
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
         const int jj = q / FM, ii = q % FM;
@@ -693,7 +707,7 @@ __device__ __forceinline__ void half16(floatx4 (&acc)[TL::FN16][TL::FM16],
         }
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-            if (q == (2 * c + 1) * NS / (2 * ND)) copy(c);
+            if (q == copy_slot<TL>(c, NC, NS)) copy(c);
         __builtin_amdgcn_sched_barrier(0);
     }
 }

@@ -71,6 +71,16 @@ def assert_fp32_bound(got, ref, Sabs, K, what=""):
         pytest.fail("%s: %d of %d outside the fp32 accumulation bound" % (what, bad.sum(), bad.size))
 
 
+def ulp_distance16(a, b):
+    """Distance in representable fp16 steps between same-shape float16
+    arrays (sign-magnitude bit patterns mapped to one ordered integer line,
+    so +0 and -0 coincide and values of opposite sign near zero are close)."""
+    def ordered(x):
+        u = np.ascontiguousarray(x).view(np.uint16).astype(np.int64)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(ordered(a) - ordered(b))
+
+
 def bits_equal(a, b):
     a = np.ascontiguousarray(a)
     b = np.ascontiguousarray(b)
@@ -465,7 +475,7 @@ def test_gemm_full_size_sampled(name, M, N, K, dist):
     ref, S = oracle.gemm_f16_points(A, B, I, J)
     assert_close(got[I, J], ref, name)
     # diagnostics on the sample: error in fp16 ulps of the oracle value
-    d = np.abs(got[I, J].view(np.uint16).astype(np.int64) - ref.view(np.uint16).astype(np.int64))
+    d = ulp_distance16(got[I, J], ref)
     say("  sample %d points: max |ulp diff| %d, frac exact %.4f" % (I.size, d.max(), np.mean(d == 0)))
     g = got[I, J].astype(np.float64)
     say("  relative Frobenius error against the exact sums: %.3e" % (np.linalg.norm(g - S) / np.linalg.norm(S)))
@@ -486,7 +496,7 @@ def test_gemm_4096_every_output_vs_oracle():
     assert not np.isnan(got).any(), "NaN left in C"
     ref, S = oracle.gemm_f16(A, B)
     assert_close(got, ref, "4096^3 every output")
-    d = np.abs(got.view(np.uint16).astype(np.int64) - ref.view(np.uint16).astype(np.int64))
+    d = ulp_distance16(got, ref)
     say("  max |ulp diff| %d, frac exact %.4f, relative Frobenius error against the exact sums %.3e"
         % (d.max(), np.mean(d == 0), np.linalg.norm(got.astype(np.float64) - S) / np.linalg.norm(S)))
     _, Sabs = oracle.gemm_f16(np.abs(A), np.abs(B))
