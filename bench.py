@@ -18,7 +18,8 @@ Then:
      hard for about 10 ms before it settles (per-launch durations of
      100 -> 130 -> 98 us), so a short run here times that transient.
   2. the secondary legs (streaming add at the default and at the pages'
-     512 x 512 blocks, x + 1, the reduction, the other GEMM configurations),
+     512 x 512 blocks, x + 1, the reduction, the other GEMM configurations,
+     and torch.matmul on the GEMM operands for context),
      each after a settle phase of back-to-back launches lasting at least
      --settle-ms, then W warm-up and K timed launches of its own;
   3. the headline: W warm-up and K timed launches of the 4096^3 GEMM,
@@ -193,6 +194,18 @@ def gemm_case(pg, ops, dist, steps, warmup, stream, settle_s=0.0, splitk=False):
                 "frac_of_peak": tflops / PEAK_FP16_TFLOPS, "settle_launches": settled,
                 "warmup": warmup, "steps": steps})
     return rec
+
+
+def vendor_case(ops, dist, steps, warmup, stream, settle_s):
+    """torch.matmul on the same fp16 operands, for context."""
+    import torch
+    tA, tB, tC = ops
+    M, K = tA.shape
+    N = tB.shape[1]
+    secs, _ = time_launches(lambda i: torch.matmul(tA, tB, out=tC), steps, warmup, stream, settle_s)
+    tflops = 2.0 * M * N * K * steps / secs / 1e12
+    return {"M": M, "N": N, "K": K, "dist": dist, "us_per_launch": round(secs / steps * 1e6, 2),
+            "tflops": round(tflops, 1)}
 
 
 def stream_case(pg, sets, steps, warmup, stream, settle_s, kind, block=None):
@@ -421,6 +434,13 @@ def main():
         print("reduction: %.1f GB/s" % out_extra["reduction"]["value"], file=sys.stderr, flush=True)
         del sets, red_sets, red_out
         others = []
+        vendor = []
+        for (M, N, Kk, dist, ops) in [(4096, 4096, 4096, "uniform", head_ops)] + other_ops[1:]:
+            vendor.append(vendor_case(ops, dist, K, W, stream, settle_s))
+        out_extra["vendor_context"] = {
+            "note": "torch.matmul (PyTorch-ROCm's fp16 GEMM, hipBLASLt) on the same device operands, "
+                    "timed the same way; context only, not part of the path",
+            "runs": vendor}
         for (M, N, Kk, dist, ops) in other_ops:
             r = gemm_case(pg, ops, dist, K, W, stream, settle_s)
             print("gemm %dx%dx%d: %.1f us, %.1f TFLOP/s" % (M, N, Kk, r["us_per_launch"], r["tflops"]),
