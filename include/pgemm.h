@@ -108,9 +108,9 @@ int pgemm_f16_num_variants(void);
 /*
  * Split-K GEMM for shapes with few output tiles and a long K (the pages'
  * parallel grid has only the output tiles to spread over the CUs, so a long
- * K leaves most CUs idle or forces small tiles).  K is cut into
- * P = pgemm's number of chunks of ceil(K/splits) rounded up to a multiple of
- * 64; chunk p runs as its own workgroups, multiplying A[:, chunk] by
+ * K leaves most CUs idle or forces small tiles).  K is cut into chunks of
+ * ceil(K/splits) rounded up to a multiple of 64, P of them non-empty
+ * (P <= splits); chunk p runs as its own workgroups, multiplying A[:, chunk] by
  * B[chunk, :] with fp32 accumulation into the fp32 partial
  * workspace[p*M*N .. (p+1)*M*N) (row-major, pitch N); a second kernel then
  * writes C = fp16_rne(W_0 + W_1 + ... + W_{P-1}), the partials added in

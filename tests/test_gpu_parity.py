@@ -269,6 +269,32 @@ def test_streaming_beyond_4gib():
         assert bits_equal(host(o[torch.from_numpy(j).to("cuda:0")]), oracle.sum_axis0_f32(pair))
 
 
+def test_sum_axis0_scalar_path_past_2_32_outputs():
+    """More than 2^32 outputs on the scalar path (n not a multiple of 4): the
+    launch caps the grid below 2^32 work-items and each lane walks several
+    outputs (grid-stride loop).  x is the index hash viewed as (2, n), the
+    second slice scaled by float32(0.3) so that the sums round; the oracle
+    sums the gathered columns."""
+    torch.cuda.empty_cache()
+    n = (1 << 32) + 3
+    rows = -(-2 * n // BIG_N_COLS)
+    say("sum axis 0 of (2, %d) f32 (%.1f GB of input)" % (n, 8e-9 * n))
+    x = inputs.hashed_f16_torch(rows, BIG_N_COLS, inputs.SEED_A, "cuda:0").view(-1)[:2 * n].float()
+    x[n:].mul_(np.float32(0.3))
+    o = pg.preduce_sum_f32(x.view(2, n))
+    rng = np.random.default_rng(9)
+    j = np.unique(np.concatenate([np.arange(2048), np.arange(n - 2048, n),
+                                  np.arange((1 << 32) - 2048, (1 << 32) + 3),
+                                  rng.integers(0, n, 16384)]))
+    a = _big_vector_at(j, inputs.SEED_A)
+    b = _big_vector_at(j + n, inputs.SEED_A) * np.float32(0.3)
+    tj = torch.from_numpy(j).to("cuda:0")
+    assert bits_equal(host(x[tj]), a) and bits_equal(host(x[tj + n]), b)
+    assert bits_equal(host(o[tj]), oracle.sum_axis0_f32(np.stack([a, b])))
+    del x, o
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------ GEMM, element by element
 
 SMALL_SHAPES = [
