@@ -174,6 +174,26 @@ def test_reduce_argument_checks(L):
     assert L.preduce_sum_f32(A, C, 1, 1 << 36, None) == EUNSUP     # 2^24 workgroups of 4096
 
 
+def test_header_compiles_as_c99_and_links(L, tmp_path):
+    """include/pgemm.h is a plain C header: a C99 program that includes it
+    compiles with gcc -pedantic, links against libpgemm.so and gets the
+    documented statuses from the host-side checks."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    exe = str(tmp_path / "c_abi_check")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(root, "include"),
+                    os.path.join(root, "tests", "c_abi_check.c"),
+                    "-L", libdir, "-lpgemm", "-Wl,-rpath," + libdir, "-o", exe], check=True)
+    res = subprocess.run([exe], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    assert "c abi ok" in res.stdout
+
+
 def test_python_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     a = torch.zeros((8, 8), dtype=torch.float16)
