@@ -63,6 +63,9 @@ def parse():
                          "launches of each kernel, for rocprofv3 runs")
     ap.add_argument("--profile-reps", type=int, default=3,
                     help="launches of each kernel in --profile mode")
+    ap.add_argument("--data-dependence", action="store_true",
+                    help="also time the 4096^3 and 8192^3 GEMMs on U[-1,1], normal(0,1/sqrt(K)) "
+                         "and all-zero operands (same instructions, different switching power)")
     ap.add_argument("--fixed-cost", action="store_true",
                     help="also time the 256x256-tile GEMM at M=N=4096 for K = 0 .. 4096 and fit "
                          "time = fixed + steps * per_step (the per-launch cost outside the K loop)")
@@ -270,6 +273,37 @@ def fixed_cost(pg, inputs, stream, settle_s):
     return {"workload": "pgemm_f16_variant 8, M=N=4096, K from 0 to 4096",
             "us_per_launch": {str(K): round(t, 2) for K, t in pts},
             "fit_K_ge_512": {"fixed_us": round(icpt, 2), "us_per_K_step_of_32": round(slope, 4)}}
+
+
+def data_dependence(pg, inputs, stream, settle_s, steps, warmup):
+    """The same GEMM launches on three operand distributions, interleaved
+    over 3 rounds (median): the kernel executes the same instructions on
+    all of them, so differences come from the chip's power limit reacting
+    to how much the operands switch."""
+    import torch
+    res = []
+    for (M, N, K) in [(4096, 4096, 4096), (8192, 8192, 8192)]:
+        ops = {}
+        for dist in ("uniform", "normal"):
+            A, B = inputs.gemm_inputs(M, N, K, dist)
+            ops[dist] = (torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda())
+        ops["zeros"] = (torch.zeros((M, K), dtype=torch.float16, device="cuda"),
+                        torch.zeros((K, N), dtype=torch.float16, device="cuda"))
+        C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        reps = max(5, steps if M == 4096 else steps // 8)
+        t = {d: [] for d in ops}
+        for _ in range(3):
+            for d, (a, b) in ops.items():
+                secs, _ = time_launches(lambda i: pg.pgemm_f16(a, b, C=C), reps, warmup, stream,
+                                        settle_s)
+                t[d].append(secs / reps)
+        for d in ops:
+            us = sorted(t[d])[1] * 1e6
+            tf = 2.0 * M * N * K / us / 1e6
+            res.append({"M": M, "N": N, "K": K, "operands": d, "us_per_launch": round(us, 2),
+                        "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_FP16_TFLOPS, 4)})
+        del ops, C
+    return res
 
 
 # ------------------------------------------------------------------ CPU baselines
@@ -485,6 +519,11 @@ def main():
                                "inside the power controller's transient"},
     }
     out.update(out_extra)
+    if args.data_dependence:
+        out["data_dependence"] = data_dependence(pg, inputs, stream, settle_s, K, W)
+        for r in out["data_dependence"]:
+            print("gemm %dx%dx%d on %s operands: %.1f TFLOP/s" % (r["M"], r["N"], r["K"], r["operands"],
+                                                                r["tflops"]), file=sys.stderr, flush=True)
     if args.fixed_cost:
         out["fixed_cost"] = fixed_cost(pg, inputs, stream, settle_s)
         print("fixed cost: %s" % out["fixed_cost"]["fit_K_ge_512"], file=sys.stderr, flush=True)
