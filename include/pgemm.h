@@ -91,8 +91,11 @@ int pgemm_f16(const void* A, const void* B, void* C,
  *   7  as 2, on the 16x16x32 matrix instruction (one instruction per 16x16
  *      output block and K step of 32 instead of two 32x32x16 ones)
  *   8  as 5, on the 16x16x32 instruction
+ *   9  as 8, persistent: at most one workgroup per compute unit, each
+ *      walking several output tiles; the copies of a tile's first steps
+ *      are issued before the previous tile's output is stored
  * Variants 1-6 give bit-identical results for the same inputs, and so do
- * variants 7-8: inside a family the grouping of the K sum of each output
+ * variants 7-9: inside a family the grouping of the K sum of each output
  * element depends neither on the tiling nor on the pipeline.  The two
  * families group the products differently (16 vs 32 per instruction), so
  * they may differ in the last bits; both are within the accuracy bound.

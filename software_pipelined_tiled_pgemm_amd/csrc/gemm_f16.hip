@@ -54,6 +54,7 @@ hipError_t launch_variant(const void* A, const void* B, void* C, int64_t M, int6
         }
         case kGemm128x128m16:
         case kGemm256x256w8m16:
+        case kGemm256x256w8m16p:
             return launch_gemm_f16_m16(A, B, C, M, N, K, variant, stream);
         case kGemmWs128x128: {
             using TL = dm::Tile<128, 128>;
@@ -89,6 +90,7 @@ int gemm_small_partner(int variant) {
         case kGemm256x256w8:
             return kGemm128x128;
         case kGemm256x256w8m16:
+        case kGemm256x256w8m16p:
             return kGemm128x128m16;
         default:
             return 0;

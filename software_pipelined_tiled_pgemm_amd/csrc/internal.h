@@ -21,7 +21,11 @@ enum GemmVariant : int {
     // results are bit-identical within this family, not with variants 1-6.
     kGemm128x128m16 = 7,    // 4 waves, 64x64 per wave, 2 workgroups per CU
     kGemm256x256w8m16 = 8,  // 8 waves (2 per SIMD), 128x64 per wave
-    kGemmNumVariants = 8,
+    // Variant 8 as a persistent kernel: one workgroup per CU walks several
+    // tiles, the next tile's first copies overlapping this tile's drain.
+    // Bit-identical to variants 7 and 8.
+    kGemm256x256w8m16p = 9,
+    kGemmNumVariants = 9,
 };
 
 // Picks a concrete variant for a problem shape: the variant measured fastest

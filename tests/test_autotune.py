@@ -122,3 +122,12 @@ def test_plan_argument_errors(L):
     h, a, b = ctypes.c_int64(), ctypes.c_int(), ctypes.c_int()
     assert L.pgemm_f16_plan(-1, 8, 8, 256, ctypes.byref(h), ctypes.byref(a), ctypes.byref(b)) == pg.PGEMM_EINVAL
     assert L.pgemm_f16_plan(8, 8, 8, 256, None, ctypes.byref(a), ctypes.byref(b)) == pg.PGEMM_EINVAL
+
+
+def test_fastest_takes_the_lowest_id_among_ties():
+    rec = {"tflops": {1: 90.0, 8: 1438.5, 9: 1441.3}}
+    assert autotune.fastest(rec) == 8      # 0.2% apart: tied
+    rec = {"tflops": {7: 952.6, 8: 1069.3, 9: 1089.9}}
+    assert autotune.fastest(rec) == 9      # 1.9% faster
+    rec = {"tflops": {2: 5.0, 3: 5.0}}
+    assert autotune.fastest(rec) == 2

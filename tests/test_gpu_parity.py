@@ -87,10 +87,10 @@ def bits_equal(a, b):
     return np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-VARIANTS = [1, 2, 3, 4, 5, 6, 7, 8]
+VARIANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9]
 # Variants that must agree bit for bit: the same matrix instruction, so the
-# same grouping of each output's K sum (32x32x16: 1-6; 16x16x32: 7-8).
-FAMILIES = [[1, 2, 3, 4, 5, 6], [7, 8]]
+# same grouping of each output's K sum (32x32x16: 1-6; 16x16x32: 7-9).
+FAMILIES = [[1, 2, 3, 4, 5, 6], [7, 8, 9]]
 
 
 # ------------------------------------------------------------ worked examples
@@ -340,6 +340,36 @@ def test_gemm_small_shapes_vs_full_oracle(M, N, K):
     for fam in FAMILIES:
         for v in fam[1:]:
             assert bits_equal(outs[fam[0]], outs[v]), "variants %d and %d differ" % (fam[0], v)
+
+
+# Variant 9 (persistent) walks several tiles per workgroup only when there
+# are more 256x256 tiles than compute units (256 on MI355X): ragged edges on
+# both sides, K below the four prologue steps, K with a tail step, and four
+# tiles per workgroup.  The next tile's first copies overlap the previous
+# tile's drain, so a race there would show as a difference from variant 8.
+@pytest.mark.parametrize("M,N,K", [(4400, 4360, 96), (4400, 4360, 200), (4136, 4616, 1048)])
+def test_persistent_variant_several_tiles_vs_oracle(M, N, K):
+    say("persistent %dx%dx%d" % (M, N, K))
+    A, B = inputs.gemm_inputs(M, N, K, seed_a=M + K, seed_b=N + K)
+    ref, _ = oracle.gemm_f16(A, B)
+    _, Sabs = oracle.gemm_f16(np.abs(A), np.abs(B))
+    got = gemm(A, B, 9)
+    assert_close(got, ref, "persistent M=%d N=%d K=%d" % (M, N, K))
+    assert_fp32_bound(got, ref, Sabs, K, "persistent M=%d N=%d K=%d" % (M, N, K))
+    assert bits_equal(got, gemm(A, B, 8)), "variants 8 and 9 differ"
+
+
+def test_persistent_variant_four_tiles_per_workgroup():
+    M = N = 8192
+    K = 520
+    say("persistent %dx%dx%d" % (M, N, K))
+    A, B = inputs.gemm_inputs(M, N, K, seed_a=95, seed_b=96)
+    tA, tB = dev(A), dev(B)
+    got9 = host(pg.pgemm_f16_variant(tA, tB, 9))
+    assert bits_equal(got9, host(pg.pgemm_f16_variant(tA, tB, 8))), "variants 8 and 9 differ"
+    rows = np.array([0, 255, 256, 4095, 4096, 8191])
+    ref, _ = oracle.gemm_f16(A[rows], B)
+    assert_close(got9[rows], ref, "persistent 8192^2 x 520, sampled rows")
 
 
 def test_gemm_special_values_all_variants():
