@@ -56,6 +56,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "internal.h"
 
@@ -470,11 +471,13 @@ __device__ __forceinline__ int bswz16(int row) { return ((row & 3) << 2) | (((ro
 __device__ __forceinline__ int aswz16(int row) { return (row >> 1) & 3; }
 
 // MF: MFMA shape, 32 (v_mfma_f32_32x32x16_f16) or 16 (v_mfma_f32_16x16x32_f16).
-template <int BM_, int BN_, int WM_ = 2, int WN_ = 2, int MF_ = 32>
+// S: stages in the LDS ring (odd, at least 5); copies run S-1 steps ahead.
+template <int BM_, int BN_, int WM_ = 2, int WN_ = 2, int MF_ = 32, int S_ = STAGES>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_;
     static constexpr int WM = WM_, WN = WN_;  // waves along M and N
     static constexpr int MF = MF_;
+    static constexpr int S = S_;
     static constexpr int T = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 32, FN = TN / 32;
@@ -485,7 +488,7 @@ struct Tile {
     static constexpr int B_BYTES = BK * BN * 2;
     static constexpr int B_ROW = BN * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int LDS = STAGES * STAGE;
+    static constexpr int LDS = S * STAGE;
     static constexpr int A_CP = A_BYTES / 1024 / (WM * WN);  // 1 KiB copies per wave per step
     static constexpr int B_CP = B_BYTES / 1024 / (WM * WN);
     static constexpr int CP = A_CP + B_CP;
@@ -494,6 +497,11 @@ struct Tile {
     static_assert(A_CP == H && B_CP == H && A_CP % 2 == 0,
                   "the copy schedule issues one operand per half-step, A in pairs");
     static_assert(LDS <= 160 * 1024, "LDS of one CU");
+    static_assert(S % 2 == 1 && S >= 5, "the copy schedule pairs aligned steps: odd S >= 5");
+    // vmcnt thresholds of the two waits of a period (see the copy schedule).
+    static constexpr int W0 = H * (2 * S - 5);
+    static constexpr int W1 = 2 * H * (S - 3);
+    static_assert(2 * H * (S - 1) < 64, "copies in flight within the vmcnt range");
     static_assert(FM * FN >= 2 * H, "every copy gets its own MFMA slot");
     static_assert(MF == 32 || (FN16 % 2 == 0 && (FN16 / 2) * FM16 >= H), "16x16x32 halves");
 };
@@ -730,7 +738,17 @@ __device__ __forceinline__ void half16(floatx4 (&acc)[TL::FN16][TL::FM16],
     }
 }
 
-__device__ __forceinline__ int wrap5(int s) { return s >= STAGES ? s - STAGES : s; }
+template <int S>
+__device__ __forceinline__ int wrap_slot(int s) { return s >= S ? s - S : s; }
+__device__ __forceinline__ int wrap5(int s) { return wrap_slot<STAGES>(s); }
+
+// f(j, slot) for the S periods j = 0 .. S-1 of one pass around a ring of S
+// (odd) slots, with the slot of period j's first step, 2j mod S, as a
+// compile-time constant.
+template <int S, class F, int... J>
+__device__ __forceinline__ void ring_pass(F&& f, std::integer_sequence<int, J...>) {
+    (f(std::integral_constant<int, J>{}, std::integral_constant<int, (2 * J) % S>{}), ...);
+}
 
 // The compute side of the pipeline: accumulators, operand fragments, the four
 // half-steps of a period and the drain, for either MFMA shape.  Call c of a
@@ -812,18 +830,27 @@ struct Compute<TL, 16> {
     }
 };
 
-// Copy schedule.  Step s lives in ring slot s mod 5.  The K loop runs in
-// periods of two steps (kt even, kt+1); a period issues the copies of steps
-// kt+4 and kt+5, one operand per half-step, H copies each:
-//   step kt,   first half:  B of kt+4
-//   step kt,   second half: A pairs 0 .. A_CP/2-1 of (kt+4, kt+5)
-//   step kt+1, first half:  A pairs A_CP/2 .. A_CP-1 of (kt+4, kt+5)
-//   step kt+1, second half: B of kt+5
-// Slot of kt+4 (= slot of kt-1) is free after the barrier in the middle of
-// step kt-1, slot of kt+5 (= slot of kt) after the one in the middle of step
-// kt, so every copy lands in a released slot.  The wait in the middle of step
-// kt covers step kt+1: for kt even its last copy (B) is 5H copies old, for kt
-// odd its last copy (an A pair's first half) is 4H+1 old.
+// Copy schedule.  Step s lives in ring slot s mod S (S odd; 5 unless the
+// tile says otherwise).  The K loop runs in periods of two steps (kt even,
+// kt+1); a period issues the copies of steps kt+S-1 and kt+S (an even and
+// an odd step, so an A pair reads the two halves of the same 128-byte
+// lines), one operand per half-step, H copies each:
+//   step kt,   first half:  B of kt+S-1
+//   step kt,   second half: A pairs 0 .. A_CP/2-1 of (kt+S-1, kt+S)
+//   step kt+1, first half:  A pairs A_CP/2 .. A_CP-1 of (kt+S-1, kt+S)
+//   step kt+1, second half: B of kt+S
+// Slot of kt+S-1 (= slot of kt-1) is free after the barrier in the middle of
+// step kt-1, slot of kt+S (= slot of kt) after the one in the middle of step
+// kt, so every copy lands in a released slot.  The prologue issues steps
+// 0 .. S-2 in the same order.  The wait in the middle of step kt covers step
+// kt+1, issued as the second step of period kt+1-S: its last copy (B) is
+// followed by the (S-3)/2 periods between (4H copies each) and the first
+// half of period kt (H), so vmcnt <= W0 = H(2S-5).  The wait in the middle of
+// step kt+1 covers step kt+2, the first step of period kt+3-S: its last copy
+// (an A pair's first half) is followed by 1 + H + 4H(S-5)/2 + 3H copies, and
+// the kernel waits for vmcnt <= W1 = 2H(S-3), one more than needed.  After
+// the prologue, step 0's last copy is followed by 2H(S-1) - 3H + 1 copies:
+// the first wait is also W0.
 //
 // SPLIT (split-K): blockIdx.y = s takes the K chunk [s*chunk, s*chunk +
 // chunk) as a sub-matrix view (A shifted by s*chunk columns with its full row
@@ -867,13 +894,13 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
             const int t = t0 + (q >> 1), h = q & 1;
             cp.issue_a(t, A, M, K, m0, (s + h) * BK, ring + (h ? sb : sa) * TL::STAGE, wave);
         };
-        // Prologue: steps 0..3, in the order a period issues them; with the
-        // steady-state copies when all four steps lie inside K.
+        // Prologue: steps 0..S-2, in the order a period issues them; with the
+        // steady-state copies when all of them lie inside K.
         cp.init_fast(A, M, m0, N, n0);
         const int64_t bstep = (int64_t)BK * N;  // elements per B step
-        if (K >= 4 * BK) {
+        if (K >= (TL::S - 1) * BK) {
 #pragma unroll
-            for (int e = 0; e < 4; e += 2) {
+            for (int e = 0; e < TL::S - 1; e += 2) {
                 const uint32_t ste = ring + e * TL::STAGE;
 #pragma unroll
                 for (int t = 0; t < H; ++t) cp.fast_b(t, B + n0 + e * bstep, ste, wave);
@@ -888,7 +915,7 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; e += 2) {
+            for (int e = 0; e < TL::S - 1; e += 2) {
 #pragma unroll
                 for (int t = 0; t < H; ++t)
                     cp.issue_b(t, B, N, K, n0, e * BK, ring + e * TL::STAGE, wave);
@@ -899,25 +926,26 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
                     cp.issue_b(t, B, N, K, n0, (e + 1) * BK, ring + (e + 1) * TL::STAGE, wave);
             }
         }
-        wait_vmcnt<5 * H>();  // this wave's copies of step 0 landed ...
-        __syncthreads();      // ... and every other wave's
+        wait_vmcnt<TL::W0>();  // this wave's copies of step 0 landed ...
+        __syncthreads();       // ... and every other wave's
         cm.first_reads(smem, wm, wn, lane);
 
         // Whole periods only: with an odd number of steps the last period's
         // second step multiplies the zeros its copies read past the end of
         // K, which leaves every accumulator unchanged (they start at +0 and
         // never become -0, so adding +0 is exact).
-        // Periods whose copies (steps kt+4, kt+5) lie inside K take the
+        // Periods whose copies (steps kt+S-1, kt+S) lie inside K take the
         // steady-state copies; the last ones, and all of a short K, the
         // general ones.  Same data either way.
-        const _Float16* b4 = B + n0 + 4 * bstep;         // rows of step kt+4
-        uint32_t a4 = 4 * BK * 2;                        // A byte offset of step kt+4
+        const _Float16* b4 = B + n0 + (TL::S - 1) * bstep;  // rows of step kt+S-1
+        uint32_t a4 = (TL::S - 1) * BK * 2;                 // A byte offset of step kt+S-1
         // One period; `slot` is the ring slot of step kt, either the run-time
         // `se` or a compile-time constant (the unrolled loop below).
         auto period = [&](int kt, auto fast, auto slot) __attribute__((always_inline)) {
             constexpr bool F = decltype(fast)::value;
             const int se = slot;
-            const int s1 = wrap5(se + 1), s2 = wrap5(se + 2), s4 = wrap5(se + 4);
+            const int s1 = wrap_slot<TL::S>(se + 1), s2 = wrap_slot<TL::S>(se + 2);
+            const int s4 = wrap_slot<TL::S>(se + TL::S - 1);  // slot of step kt+S-1
             const char* cur = smem + se * TL::STAGE;
             const char* nxt = smem + s1 * TL::STAGE;
             const uint32_t st4 = ring + s4 * TL::STAGE, st5 = ring + se * TL::STAGE;
@@ -926,18 +954,18 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
                     const int h = q & 1;
                     cp.fast_a(t0 + (q >> 1), a4 + h * (BK * 2), h ? st5 : st4, wave);
                 } else {
-                    a_pairs(q, t0, kt + 4, s4, se);
+                    a_pairs(q, t0, kt + TL::S - 1, s4, se);
                 }
             };
-            // first half of step kt; B of step kt+4
+            // first half of step kt; B of step kt+S-1
             cm.template half<0, H>(cur, wm, wn, lane, [&](int q) __attribute__((always_inline)) {
                 if constexpr (F)
                     cp.fast_b(q, b4, st4, wave);
                 else
-                    cp.issue_b(q, B, N, K, n0, (kt + 4) * BK, st4, wave);
+                    cp.issue_b(q, B, N, K, n0, (kt + TL::S - 1) * BK, st4, wave);
             });
             // copy_wait for step kt+1; the barrier also releases slot se
-            wait_vmcnt<5 * H>();
+            wait_vmcnt<TL::W0>();
             __syncthreads();
             if constexpr (PGEMM_POISON_LDS) {
                 poison_stage<TL::STAGE, TL::T>(smem + se * TL::STAGE, tid);
@@ -951,37 +979,37 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
                 pairs(q, TL::A_CP / 2);
             });
             // copy_wait for step kt+2; the barrier also releases slot s1
-            wait_vmcnt<4 * H>();
+            wait_vmcnt<TL::W1>();
             __syncthreads();
             if constexpr (PGEMM_POISON_LDS) {
                 poison_stage<TL::STAGE, TL::T>(smem + s1 * TL::STAGE, tid);
                 __syncthreads();
             }
-            // second half of step kt+1 (reads of step kt+2 begin); B of step kt+5
+            // second half of step kt+1 (reads of step kt+2 begin); B of step kt+S
             cm.template half<3, H>(smem + s2 * TL::STAGE, wm, wn, lane,
                                    [&](int q) __attribute__((always_inline)) {
                                        if constexpr (F)
                                            cp.fast_b(q, b4 + bstep, st5, wave);
                                        else
-                                           cp.issue_b(q, B, N, K, n0, (kt + 5) * BK, st5, wave);
+                                           cp.issue_b(q, B, N, K, n0, (kt + TL::S) * BK, st5,
+                                                      wave);
                                    });
             b4 += 2 * bstep;
             a4 += 2 * BK * 2;
             return s2;
         };
-        using std::integral_constant;
-        const int fast_end = K / BK - 5;  // kt < fast_end <=> step kt+5 is a full step
+        constexpr int S = TL::S;
+        const int fast_end = K / BK - S;  // kt < fast_end <=> step kt+S is a full step
         int kt = 0;
-        // Five periods (ten steps) bring the ring back to slot 0, so the
+        // S periods (2S steps) bring the ring back to slot 0, so the
         // unrolled loop knows every slot at compile time: no slot arithmetic
         // between the MFMAs.
-        for (; kt + 8 < fast_end && kt + 8 < nk; kt += 10) {
-            period(kt, std::true_type{}, integral_constant<int, 0>{});
-            period(kt + 2, std::true_type{}, integral_constant<int, 2>{});
-            period(kt + 4, std::true_type{}, integral_constant<int, 4>{});
-            period(kt + 6, std::true_type{}, integral_constant<int, 1>{});
-            period(kt + 8, std::true_type{}, integral_constant<int, 3>{});
-        }
+        for (; kt + 2 * (S - 1) < fast_end && kt + 2 * (S - 1) < nk; kt += 2 * S)
+            ring_pass<S>(
+                [&](auto j, auto slot) __attribute__((always_inline)) {
+                    period(kt + 2 * decltype(j)::value, std::true_type{}, slot);
+                },
+                std::make_integer_sequence<int, S>{});
         // The tail periods recompute the per-lane copy offsets instead of
         // keeping them live across the unrolled loop (same values; the empty
         // statement hides that from the compiler).
@@ -1013,20 +1041,6 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
         cm.drain_c(smem, C, M, N, m0, n0, tid_d, wm, wn);
 }
 
-// Persistent form of `kernel` (no split-K): a grid of at most one workgroup
-// per CU walks the logical tiles blockIdx.x, blockIdx.x + stride, ...
-// (stride = the grid size, a multiple of 8, which keeps the XCD-aware map
-// of tile_of_block).  Right after a tile's K loop the copies of the next
-// tile's steps 0-3 go into ring slots 0-3, and the finished tile is drained
-// through slot 4 in bands of rows (drain_bands), so the next tile's operands
-// are in flight while this tile is converted and stored.  The next tile's
-// first wait (vmcnt <= 5H) then also covers the drain's stores, which were
-// issued after those copies: vector memory operations complete in issue
-// order, so all but the 5H youngest are done, steps 0 and 1 among them.
-// Per-lane values are derived afresh in every tile (from an opaque copy of
-// the thread index), so none is kept live across the K loop beyond what
-// `kernel` keeps.  A separate kernel, so that the one-tile kernel's code is
-// unchanged.
 // The kernel arguments as they lie in the argument segment (each at its
 // natural alignment).
 struct KernelArgs {
@@ -1042,6 +1056,20 @@ static_assert(offsetof(KernelArgs, M) == 24 && offsetof(KernelArgs, group_m) == 
                   offsetof(KernelArgs, W) == 48 && offsetof(KernelArgs, stride) == 56,
               "the argument layout of the GEMM kernels");
 
+// Persistent form of `kernel` (no split-K): a grid of at most one workgroup
+// per CU walks the logical tiles blockIdx.x, blockIdx.x + stride, ...
+// (stride = the grid size, a multiple of 8, which keeps the XCD-aware map
+// of tile_of_block).  Right after a tile's K loop the copies of the next
+// tile's steps 0..S-2 go into ring slots 0..S-2, and the finished tile is drained
+// through slot S-1 in bands of rows (drain_bands), so the next tile's
+// operands are in flight while this tile is converted and stored.  The next
+// tile's first wait (vmcnt <= W0) then also covers the drain's stores, which
+// were issued after those copies: vector memory operations complete in issue
+// order, so all but the W0 youngest are done, step 0 among them.
+// Per-lane values are derived afresh in every tile (from an opaque copy of
+// the thread index), so none is kept live across the K loop beyond what
+// `kernel` keeps.  A separate kernel, so that the one-tile kernel's code is
+// unchanged.
 template <class TL, int WPE>
 __global__ __launch_bounds__(TL::T, 1) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict__,
@@ -1095,14 +1123,15 @@ void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict_
             const int t = t0 + (q >> 1), h = q & 1;
             c.issue_a(t, A, M, K, pm0, (s + h) * BK, ring + (h ? sb : sa) * TL::STAGE, wave);
         };
-        // Steps 0..3 of the tile at (pm0, pn0) into slots 0..3, as in `kernel`.
+        // Steps 0..S-2 of the tile at (pm0, pn0) into slots 0..S-2, as in
+        // `kernel`.
         auto prologue = [&](int pl, int pm0, int pn0) __attribute__((always_inline)) {
             Copier<TL> c;
             c.init(pl, wave, K, N, pn0);
             c.init_fast(A, M, pm0, N, pn0);
-            if (K >= 4 * BK) {
+            if (K >= (TL::S - 1) * BK) {
 #pragma unroll
-                for (int e = 0; e < 4; e += 2) {
+                for (int e = 0; e < TL::S - 1; e += 2) {
                     const uint32_t ste = ring + e * TL::STAGE;
 #pragma unroll
                     for (int t = 0; t < H; ++t) c.fast_b(t, B + pn0 + e * bstep, ste, wave);
@@ -1118,7 +1147,7 @@ void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict_
                 }
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; e += 2) {
+                for (int e = 0; e < TL::S - 1; e += 2) {
 #pragma unroll
                     for (int t = 0; t < H; ++t)
                         c.issue_b(t, B, N, K, pn0, e * BK, ring + e * TL::STAGE, wave);
@@ -1138,16 +1167,17 @@ void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict_
             Copier<TL> cp;
             cp.init(lane, wave, K, N, n0);
             cp.init_fast(A, M, m0, N, n0);
-            wait_vmcnt<5 * H>();  // this wave's copies of step 0 landed ...
-            __syncthreads();      // ... and every other wave's
+            wait_vmcnt<TL::W0>();  // this wave's copies of step 0 landed ...
+            __syncthreads();       // ... and every other wave's
             cm.first_reads(smem, wm, wn, lane);
             // The K loop of `kernel`, unchanged.
-            const _Float16* b4 = B + n0 + 4 * bstep;
-            uint32_t a4 = 4 * BK * 2;
+            const _Float16* b4 = B + n0 + (TL::S - 1) * bstep;
+            uint32_t a4 = (TL::S - 1) * BK * 2;
             auto period = [&](int kt, auto fast, auto slot) __attribute__((always_inline)) {
                 constexpr bool F = decltype(fast)::value;
                 const int se = slot;
-                const int s1 = wrap5(se + 1), s2 = wrap5(se + 2), s4 = wrap5(se + 4);
+                const int s1 = wrap_slot<TL::S>(se + 1), s2 = wrap_slot<TL::S>(se + 2);
+                const int s4 = wrap_slot<TL::S>(se + TL::S - 1);
                 const char* cur = smem + se * TL::STAGE;
                 const char* nxt = smem + s1 * TL::STAGE;
                 const uint32_t st4 = ring + s4 * TL::STAGE, st5 = ring + se * TL::STAGE;
@@ -1156,16 +1186,16 @@ void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict_
                         const int h = q & 1;
                         cp.fast_a(t0 + (q >> 1), a4 + h * (BK * 2), h ? st5 : st4, wave);
                     } else {
-                        a_pairs(cp, m0, q, t0, kt + 4, s4, se);
+                        a_pairs(cp, m0, q, t0, kt + TL::S - 1, s4, se);
                     }
                 };
                 cm.template half<0, H>(cur, wm, wn, lane, [&](int q) __attribute__((always_inline)) {
                     if constexpr (F)
                         cp.fast_b(q, b4, st4, wave);
                     else
-                        cp.issue_b(q, B, N, K, n0, (kt + 4) * BK, st4, wave);
+                        cp.issue_b(q, B, N, K, n0, (kt + TL::S - 1) * BK, st4, wave);
                 });
-                wait_vmcnt<5 * H>();
+                wait_vmcnt<TL::W0>();
                 __syncthreads();
                 if constexpr (PGEMM_POISON_LDS) {
                     poison_stage<TL::STAGE, TL::T>(smem + se * TL::STAGE, opaque_tid());
@@ -1176,7 +1206,7 @@ void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict_
                 cm.template half<2, H>(nxt, wm, wn, lane, [&](int q) __attribute__((always_inline)) {
                     pairs(q, TL::A_CP / 2);
                 });
-                wait_vmcnt<4 * H>();
+                wait_vmcnt<TL::W1>();
                 __syncthreads();
                 if constexpr (PGEMM_POISON_LDS) {
                     poison_stage<TL::STAGE, TL::T>(smem + s1 * TL::STAGE, opaque_tid());
@@ -1187,23 +1217,22 @@ void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict_
                                            if constexpr (F)
                                                cp.fast_b(q, b4 + bstep, st5, wave);
                                            else
-                                               cp.issue_b(q, B, N, K, n0, (kt + 5) * BK, st5,
-                                                          wave);
+                                               cp.issue_b(q, B, N, K, n0, (kt + TL::S) * BK,
+                                                          st5, wave);
                                        });
                 b4 += 2 * bstep;
                 a4 += 2 * BK * 2;
                 return s2;
             };
-            using std::integral_constant;
-            const int fast_end = K / BK - 5;
+            constexpr int S = TL::S;
+            const int fast_end = K / BK - S;
             int kt = 0;
-            for (; kt + 8 < fast_end && kt + 8 < nk; kt += 10) {
-                period(kt, std::true_type{}, integral_constant<int, 0>{});
-                period(kt + 2, std::true_type{}, integral_constant<int, 2>{});
-                period(kt + 4, std::true_type{}, integral_constant<int, 4>{});
-                period(kt + 6, std::true_type{}, integral_constant<int, 1>{});
-                period(kt + 8, std::true_type{}, integral_constant<int, 3>{});
-            }
+            for (; kt + 2 * (S - 1) < fast_end && kt + 2 * (S - 1) < nk; kt += 2 * S)
+                ring_pass<S>(
+                    [&](auto j, auto slot) __attribute__((always_inline)) {
+                        period(kt + 2 * decltype(j)::value, std::true_type{}, slot);
+                    },
+                    std::make_integer_sequence<int, S>{});
             cp.init(opaque_tid() & 63, wave, K, N, n0);
             int se = 0;
             for (; kt < fast_end && kt < nk; kt += 2) se = period(kt, std::true_type{}, se);
@@ -1224,7 +1253,7 @@ void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict_
             n0 = tn * TL::BN;
             if (nk > 0) prologue(tid_d & 63, m0, n0);
         }
-        cm.drain_bands(smem + (STAGES - 1) * TL::STAGE, h->C, M, N, dm0, dn0, tid_d, wm, wn);
+        cm.drain_bands(smem + (TL::S - 1) * TL::STAGE, h->C, M, N, dm0, dn0, tid_d, wm, wn);
         if (!more) break;
     }
 }
