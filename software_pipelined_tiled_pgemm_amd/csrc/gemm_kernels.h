@@ -1041,20 +1041,16 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
         cm.drain_c(smem, C, M, N, m0, n0, tid_d, wm, wn);
 }
 
-// The kernel arguments as they lie in the argument segment (each at its
-// natural alignment).
-struct KernelArgs {
+// Arguments of the persistent kernel, passed as its only (by-value)
+// argument, so that they are also the first bytes of its argument segment.
+struct PersistentArgs {
     const _Float16* A;
     const _Float16* B;
     _Float16* C;
     int M, N, K, tiles_m, tiles_n, group_m;
-    float* W;
-    int stride;
+    int stride;  // the grid size
 };
-typedef const __attribute__((address_space(4))) KernelArgs ConstKernelArgs;
-static_assert(offsetof(KernelArgs, M) == 24 && offsetof(KernelArgs, group_m) == 44 &&
-                  offsetof(KernelArgs, W) == 48 && offsetof(KernelArgs, stride) == 56,
-              "the argument layout of the GEMM kernels");
+typedef const __attribute__((address_space(4))) PersistentArgs ConstPersistentArgs;
 
 // Persistent form of `kernel` (no split-K): a grid of at most one workgroup
 // per CU walks the logical tiles blockIdx.x, blockIdx.x + stride, ...
@@ -1072,9 +1068,7 @@ static_assert(offsetof(KernelArgs, M) == 24 && offsetof(KernelArgs, group_m) == 
 // unchanged.
 template <class TL, int WPE>
 __global__ __launch_bounds__(TL::T, 1) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict__,
-                       _Float16* __restrict__, int, int, int, int, int, int, float* __restrict__,
-                       int) {
+void kernel_persistent(const PersistentArgs) {
     __shared__ __attribute__((aligned(1024))) char smem[TL::LDS];
     constexpr int H = TL::H;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1089,9 +1083,10 @@ void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict_
     // needs them, through an opaque copy of the segment address, so that
     // none of them (nor anything derived from them) occupies a register
     // across the K loop, which runs at the register limit.
-    ConstKernelArgs* const args = (ConstKernelArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    ConstPersistentArgs* const args =
+        (ConstPersistentArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     auto load_args = [&]() __attribute__((always_inline)) {
-        ConstKernelArgs* p = args;
+        ConstPersistentArgs* p = args;
         asm volatile("" : "+s"(p));
         return p;
     };
@@ -1099,7 +1094,7 @@ void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict_
     int blk = blockIdx.x;
     int m0, n0;
     {
-        ConstKernelArgs* g = load_args();
+        ConstPersistentArgs* g = load_args();
         int tm, tn;
         tile_of_block(blk, g->tiles_m * g->tiles_n, g->tiles_m, g->tiles_n, g->group_m, tm, tn);
         m0 = tm * TL::BM;
@@ -1108,7 +1103,7 @@ void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict_
 
     Compute<TL> cm;
     for (bool first = true;; first = false) {
-        ConstKernelArgs* g = load_args();
+        ConstPersistentArgs* g = load_args();
         const int M = g->M, N = g->N, K = g->K;
         const _Float16* const A = g->A;
         const _Float16* const B = g->B;
@@ -1242,7 +1237,7 @@ void kernel_persistent(const _Float16* __restrict__, const _Float16* __restrict_
         __syncthreads();  // every wave is done with the stage ring
         const int tid_d = opaque_tid();
         const int dm0 = m0, dn0 = n0;
-        ConstKernelArgs* h = load_args();
+        ConstPersistentArgs* h = load_args();
         const int ntiles = h->tiles_m * h->tiles_n;
         blk += h->stride;
         const bool more = blk < ntiles;
@@ -1663,11 +1658,17 @@ hipError_t launch_persistent(KernelFn kern, int threads, const void* A, const vo
     if (grid > nwg) grid = nwg;
     if (grid < 1) grid = 1;
     const int group_m = tiles_m < 4 ? tiles_m : 4;
-    float* const nows = nullptr;
-    hipLaunchKernelGGL(kern, dim3(grid, 1), dim3(threads), 0, stream,
-                       static_cast<const _Float16*>(A), static_cast<const _Float16*>(B),
-                       static_cast<_Float16*>(C), (int)M, (int)N, (int)K, tiles_m, tiles_n, group_m,
-                       nows, grid);
+    const dm::PersistentArgs args = {static_cast<const _Float16*>(A),
+                                     static_cast<const _Float16*>(B),
+                                     static_cast<_Float16*>(C),
+                                     (int)M,
+                                     (int)N,
+                                     (int)K,
+                                     tiles_m,
+                                     tiles_n,
+                                     group_m,
+                                     grid};
+    hipLaunchKernelGGL(kern, dim3(grid, 1), dim3(threads), 0, stream, args);
     return hipGetLastError();
 }
 }  // namespace
