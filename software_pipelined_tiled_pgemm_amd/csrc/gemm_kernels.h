@@ -16,11 +16,12 @@
 //  * copy_start early / copy_wait late with several buffers (Pallas
 //    software-pipelining guide, section 4; max_concurrent_steps of the
 //    quickstart's emit_pipeline).  Two pipelines are implemented:
-//      - LDS-DMA pipeline (variants 1, 2, 5, 7, 8): a ring of 5 LDS stages of
-//        BK = 32.  copy_start is a buffer_load ... lds (global memory
-//        straight into LDS, no registers), issued 2 to 4 steps ahead and
-//        spread over the MFMA slots; copy_wait is an s_waitcnt on this
-//        wave's own copies followed by the workgroup barrier.
+//      - LDS-DMA pipeline (variants 1, 2, 5, 7, 8, and 9, its persistent
+//        form): a ring of 5 LDS stages of BK = 32.  copy_start is a
+//        buffer_load ... lds (global memory straight into LDS, no
+//        registers), issued 2 to 4 steps ahead and spread over the MFMA
+//        slots; copy_wait is an s_waitcnt on this wave's own copies followed
+//        by the workgroup barrier.
 //      - register-staged pipeline (variants 3, 4): 2 LDS stages of BK = 64
 //        plus one register stage; global loads for step k+2 are in flight
 //        while step k computes.
@@ -32,12 +33,12 @@
 //    MFMA blocks held in VGPR/AGPR for the whole K loop, zeroed before step 0
 //    (the initialise-before-accumulate rule of the guide, section 7.2).
 //  * Drain (quickstart's epilogue: cast, stage through shared memory, copy
-//    out): fp32 -> fp16, written to LDS, then 16-byte coalesced non-temporal
-//    row stores.
+//    out): fp32 -> fp16, written to LDS (the whole tile, or bands of rows
+//    on the 16x16x32 path), then 16-byte coalesced non-temporal row stores.
 //
 // Matrix instructions: v_mfma_f32_32x32x16_f16 (variants 1-6: 32x32 output
 // block, 16-deep K, 8 fp16 per lane per operand; lanes 0-31 carry K 0..7,
-// lanes 32-63 K 8..15) and v_mfma_f32_16x16x32_f16 (variants 7, 8: 16x16
+// lanes 32-63 K 8..15) and v_mfma_f32_16x16x32_f16 (variants 7-9: 16x16
 // block, the whole K 32 of a stage; see Compute<TL, 16>).  Each MFMA computes
 // the transposed block C^T = B^T A^T (B^T as the row operand), so that each
 // lane ends up holding four consecutive columns of one row of C -- 8

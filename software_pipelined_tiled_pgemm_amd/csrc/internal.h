@@ -23,7 +23,7 @@ enum GemmVariant : int {
     kGemm256x256w8m16 = 8,  // 8 waves (2 per SIMD), 128x64 per wave
     // Variant 8 as a persistent kernel: one workgroup per CU walks several
     // tiles, the next tile's first copies overlapping this tile's drain.
-    // Bit-identical to variants 7 and 8.
+    // Bit-identical to variants 7 and 8 (the same K order).
     kGemm256x256w8m16p = 9,
     kGemmNumVariants = 9,
 };
