@@ -25,13 +25,24 @@ __all__ = [
 ]
 
 
+# torch and the few of its entry points each call uses, looked up once: a
+# small GEMM's kernel takes about 5 us, so the binding's own per-call work
+# (argument checks, stream lookup, the ctypes call) has to stay below that.
 _TORCH = None
+_TENSOR = None
+_F16 = None
+_F32 = None
+_CUR_DEVICE = None
+_RAW_STREAM = None
 
 
 def _torch():
-    global _TORCH
+    global _TORCH, _TENSOR, _F16, _F32, _CUR_DEVICE, _RAW_STREAM
     if _TORCH is None:
         import torch
+        _TENSOR, _F16, _F32 = torch.Tensor, torch.float16, torch.float32
+        _CUR_DEVICE = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
         _TORCH = torch
     return _TORCH
 
@@ -41,19 +52,18 @@ def _raw_stream(index, stream):
     stream of device `index`."""
     if stream is not None:
         return stream.cuda_stream
-    torch = _torch()
-    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-    if get is not None:
-        return get(index)
-    return torch.cuda.current_stream(index).cuda_stream
+    if _RAW_STREAM is not None:
+        return _RAW_STREAM(index)
+    return _torch().cuda.current_stream(index).cuda_stream
 
 
 def _invoke(t, stream, fn):
-    """fn(stream handle) with t's device current.  The per-call cost matters
-    for small problems, so the device is switched only when it differs."""
+    """fn(stream handle) with t's device current, switched only when it
+    differs.  Device tensors exist, so the HIP runtime is initialised and the
+    current device can be read directly."""
     torch = _torch()
     index = t.get_device()
-    if index == torch.cuda.current_device():
+    if index == _CUR_DEVICE():
         return fn(_raw_stream(index, stream))
     with torch.cuda.device(index):
         return fn(_raw_stream(index, stream))
@@ -61,6 +71,10 @@ def _invoke(t, stream, fn):
 
 def _check_dev(t, dtype, name, ndim=None):
     torch = _torch()
+    # the common case in one expression; the branches below name the problem
+    if (type(t) is _TENSOR and t.is_cuda and t.dtype is dtype
+            and (ndim is None or t.dim() == ndim) and t.is_contiguous()):
+        return
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if not t.is_cuda:
