@@ -831,6 +831,111 @@ struct Compute<TL, 16> {
     }
 };
 
+// The K loop of one tile: from the wait for step 0 (the prologue has issued
+// the copies of steps 0 .. S-2 into slots 0 .. S-2) to the end of the copies
+// past K.  a_pairs(q, t0, s, sa, sb): the general A copies of pair unit q,
+// starting at copy t0, of steps (s, s+1) into slots (sa, sb); relane(): the
+// lane index, recomputed; ptid(): the thread index (race-detection build).
+template <class TL, class APairs, class Relane, class PTid>
+__device__ __forceinline__ void k_loop(Compute<TL>& cm, Copier<TL>& cp, char* smem, uint32_t ring,
+                                       const _Float16* B, int N, int K, int lda, int n0, int nk,
+                                       int64_t bstep, int wm, int wn, int lane, int wave,
+                                       APairs&& a_pairs, Relane&& relane, PTid&& ptid) {
+    constexpr int H = TL::H;
+    wait_vmcnt<TL::W0>();  // this wave's copies of step 0 landed ...
+    __syncthreads();       // ... and every other wave's
+    cm.first_reads(smem, wm, wn, lane);
+
+    // Whole periods only: with an odd number of steps the last period's
+    // second step multiplies the zeros its copies read past the end of
+    // K, which leaves every accumulator unchanged (they start at +0 and
+    // never become -0, so adding +0 is exact).
+    // Periods whose copies (steps kt+S-1, kt+S) lie inside K take the
+    // steady-state copies; the last ones, and all of a short K, the
+    // general ones.  Same data either way.
+    const _Float16* b4 = B + n0 + (TL::S - 1) * bstep;  // rows of step kt+S-1
+    uint32_t a4 = (TL::S - 1) * BK * 2;                 // A byte offset of step kt+S-1
+    // One period; `slot` is the ring slot of step kt, either the run-time
+    // `se` or a compile-time constant (the unrolled loop below).
+    auto period = [&](int kt, auto fast, auto slot) __attribute__((always_inline)) {
+        constexpr bool F = decltype(fast)::value;
+        const int se = slot;
+        const int s1 = wrap_slot<TL::S>(se + 1), s2 = wrap_slot<TL::S>(se + 2);
+        const int s4 = wrap_slot<TL::S>(se + TL::S - 1);  // slot of step kt+S-1
+        const char* cur = smem + se * TL::STAGE;
+        const char* nxt = smem + s1 * TL::STAGE;
+        const uint32_t st4 = ring + s4 * TL::STAGE, st5 = ring + se * TL::STAGE;
+        auto pairs = [&](int q, int t0) __attribute__((always_inline)) {
+            if constexpr (F) {
+                const int h = q & 1;
+                cp.fast_a(t0 + (q >> 1), a4 + h * (BK * 2), h ? st5 : st4, wave);
+            } else {
+                a_pairs(q, t0, kt + TL::S - 1, s4, se);
+            }
+        };
+        // first half of step kt; B of step kt+S-1
+        cm.template half<0, H>(cur, wm, wn, lane, [&](int q) __attribute__((always_inline)) {
+            if constexpr (F)
+                cp.fast_b(q, b4, st4, wave);
+            else
+                cp.issue_b(q, B, N, K, n0, (kt + TL::S - 1) * BK, st4, wave);
+        });
+        // copy_wait for step kt+1; the barrier also releases slot se
+        wait_vmcnt<TL::W0>();
+        __syncthreads();
+        if constexpr (PGEMM_POISON_LDS) {
+            poison_stage<TL::STAGE, TL::T>(smem + se * TL::STAGE, ptid());
+            __syncthreads();
+        }
+        // second half of step kt (reads of step kt+1 begin); first A pairs
+        cm.template half<1, H>(nxt, wm, wn, lane,
+                               [&](int q) __attribute__((always_inline)) { pairs(q, 0); });
+        // first half of step kt+1; other A pairs
+        cm.template half<2, H>(nxt, wm, wn, lane, [&](int q) __attribute__((always_inline)) {
+            pairs(q, TL::A_CP / 2);
+        });
+        // copy_wait for step kt+2; the barrier also releases slot s1
+        wait_vmcnt<TL::W1>();
+        __syncthreads();
+        if constexpr (PGEMM_POISON_LDS) {
+            poison_stage<TL::STAGE, TL::T>(smem + s1 * TL::STAGE, ptid());
+            __syncthreads();
+        }
+        // second half of step kt+1 (reads of step kt+2 begin); B of step kt+S
+        cm.template half<3, H>(smem + s2 * TL::STAGE, wm, wn, lane,
+                               [&](int q) __attribute__((always_inline)) {
+                                   if constexpr (F)
+                                       cp.fast_b(q, b4 + bstep, st5, wave);
+                                   else
+                                       cp.issue_b(q, B, N, K, n0, (kt + TL::S) * BK, st5,
+                                                  wave);
+                               });
+        b4 += 2 * bstep;
+        a4 += 2 * BK * 2;
+        return s2;
+    };
+    constexpr int S = TL::S;
+    const int fast_end = K / BK - S;  // kt < fast_end <=> step kt+S is a full step
+    int kt = 0;
+    // S periods (2S steps) bring the ring back to slot 0, so the
+    // unrolled loop knows every slot at compile time: no slot arithmetic
+    // between the MFMAs.
+    for (; kt + 2 * (S - 1) < fast_end && kt + 2 * (S - 1) < nk; kt += 2 * S)
+        ring_pass<S>(
+            [&](auto j, auto slot) __attribute__((always_inline)) {
+                period(kt + 2 * decltype(j)::value, std::true_type{}, slot);
+            },
+            std::make_integer_sequence<int, S>{});
+    // The tail periods recompute the per-lane copy offsets (relane: the same
+    // lane index, hidden from the compiler) instead of keeping them live
+    // across the unrolled loop.
+    cp.init(relane(), wave, lda, N, n0);
+    int se = 0;  // slot of step kt
+    for (; kt < fast_end && kt < nk; kt += 2) se = period(kt, std::true_type{}, se);
+    for (; kt < nk; kt += 2) se = period(kt, std::false_type{}, se);
+    wait_vmcnt<0>();  // drain the copies of the steps past the end
+}
+
 // Copy schedule.  Step s lives in ring slot s mod S (S odd; 5 unless the
 // tile says otherwise).  The K loop runs in periods of two steps (kt even,
 // kt+1); a period issues the copies of steps kt+S-1 and kt+S (an even and
@@ -927,102 +1032,13 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
                     cp.issue_b(t, B, N, K, n0, (e + 1) * BK, ring + (e + 1) * TL::STAGE, wave);
             }
         }
-        wait_vmcnt<TL::W0>();  // this wave's copies of step 0 landed ...
-        __syncthreads();       // ... and every other wave's
-        cm.first_reads(smem, wm, wn, lane);
-
-        // Whole periods only: with an odd number of steps the last period's
-        // second step multiplies the zeros its copies read past the end of
-        // K, which leaves every accumulator unchanged (they start at +0 and
-        // never become -0, so adding +0 is exact).
-        // Periods whose copies (steps kt+S-1, kt+S) lie inside K take the
-        // steady-state copies; the last ones, and all of a short K, the
-        // general ones.  Same data either way.
-        const _Float16* b4 = B + n0 + (TL::S - 1) * bstep;  // rows of step kt+S-1
-        uint32_t a4 = (TL::S - 1) * BK * 2;                 // A byte offset of step kt+S-1
-        // One period; `slot` is the ring slot of step kt, either the run-time
-        // `se` or a compile-time constant (the unrolled loop below).
-        auto period = [&](int kt, auto fast, auto slot) __attribute__((always_inline)) {
-            constexpr bool F = decltype(fast)::value;
-            const int se = slot;
-            const int s1 = wrap_slot<TL::S>(se + 1), s2 = wrap_slot<TL::S>(se + 2);
-            const int s4 = wrap_slot<TL::S>(se + TL::S - 1);  // slot of step kt+S-1
-            const char* cur = smem + se * TL::STAGE;
-            const char* nxt = smem + s1 * TL::STAGE;
-            const uint32_t st4 = ring + s4 * TL::STAGE, st5 = ring + se * TL::STAGE;
-            auto pairs = [&](int q, int t0) __attribute__((always_inline)) {
-                if constexpr (F) {
-                    const int h = q & 1;
-                    cp.fast_a(t0 + (q >> 1), a4 + h * (BK * 2), h ? st5 : st4, wave);
-                } else {
-                    a_pairs(q, t0, kt + TL::S - 1, s4, se);
-                }
-            };
-            // first half of step kt; B of step kt+S-1
-            cm.template half<0, H>(cur, wm, wn, lane, [&](int q) __attribute__((always_inline)) {
-                if constexpr (F)
-                    cp.fast_b(q, b4, st4, wave);
-                else
-                    cp.issue_b(q, B, N, K, n0, (kt + TL::S - 1) * BK, st4, wave);
-            });
-            // copy_wait for step kt+1; the barrier also releases slot se
-            wait_vmcnt<TL::W0>();
-            __syncthreads();
-            if constexpr (PGEMM_POISON_LDS) {
-                poison_stage<TL::STAGE, TL::T>(smem + se * TL::STAGE, tid);
-                __syncthreads();
-            }
-            // second half of step kt (reads of step kt+1 begin); first A pairs
-            cm.template half<1, H>(nxt, wm, wn, lane,
-                                   [&](int q) __attribute__((always_inline)) { pairs(q, 0); });
-            // first half of step kt+1; other A pairs
-            cm.template half<2, H>(nxt, wm, wn, lane, [&](int q) __attribute__((always_inline)) {
-                pairs(q, TL::A_CP / 2);
-            });
-            // copy_wait for step kt+2; the barrier also releases slot s1
-            wait_vmcnt<TL::W1>();
-            __syncthreads();
-            if constexpr (PGEMM_POISON_LDS) {
-                poison_stage<TL::STAGE, TL::T>(smem + s1 * TL::STAGE, tid);
-                __syncthreads();
-            }
-            // second half of step kt+1 (reads of step kt+2 begin); B of step kt+S
-            cm.template half<3, H>(smem + s2 * TL::STAGE, wm, wn, lane,
-                                   [&](int q) __attribute__((always_inline)) {
-                                       if constexpr (F)
-                                           cp.fast_b(q, b4 + bstep, st5, wave);
-                                       else
-                                           cp.issue_b(q, B, N, K, n0, (kt + TL::S) * BK, st5,
-                                                      wave);
-                                   });
-            b4 += 2 * bstep;
-            a4 += 2 * BK * 2;
-            return s2;
-        };
-        constexpr int S = TL::S;
-        const int fast_end = K / BK - S;  // kt < fast_end <=> step kt+S is a full step
-        int kt = 0;
-        // S periods (2S steps) bring the ring back to slot 0, so the
-        // unrolled loop knows every slot at compile time: no slot arithmetic
-        // between the MFMAs.
-        for (; kt + 2 * (S - 1) < fast_end && kt + 2 * (S - 1) < nk; kt += 2 * S)
-            ring_pass<S>(
-                [&](auto j, auto slot) __attribute__((always_inline)) {
-                    period(kt + 2 * decltype(j)::value, std::true_type{}, slot);
-                },
-                std::make_integer_sequence<int, S>{});
-        // The tail periods recompute the per-lane copy offsets instead of
-        // keeping them live across the unrolled loop (same values; the empty
-        // statement hides that from the compiler).
-        {
-            int l = lane;
-            asm volatile("" : "+v"(l));
-            cp.init(l, wave, Kfull, N, n0);
-        }
-        int se = 0;  // slot of step kt
-        for (; kt < fast_end && kt < nk; kt += 2) se = period(kt, std::true_type{}, se);
-        for (; kt < nk; kt += 2) se = period(kt, std::false_type{}, se);
-        wait_vmcnt<0>();  // drain the copies of the steps past the end
+        k_loop<TL>(cm, cp, smem, ring, B, N, K, Kfull, n0, nk, bstep, wm, wn, lane, wave, a_pairs,
+                   [&]() __attribute__((always_inline)) {
+                       int l = lane;
+                       asm volatile("" : "+v"(l));
+                       return l;
+                   },
+                   [&]() __attribute__((always_inline)) { return tid; });
     }
     __syncthreads();  // every wave is done with the stage ring
     // The drain derives its lane addresses from the thread index afresh (the
@@ -1163,77 +1179,13 @@ void kernel_persistent(const PersistentArgs) {
             Copier<TL> cp;
             cp.init(lane, wave, K, N, n0);
             cp.init_fast(A, M, m0, N, n0);
-            wait_vmcnt<TL::W0>();  // this wave's copies of step 0 landed ...
-            __syncthreads();       // ... and every other wave's
-            cm.first_reads(smem, wm, wn, lane);
-            // The K loop of `kernel`, unchanged.
-            const _Float16* b4 = B + n0 + (TL::S - 1) * bstep;
-            uint32_t a4 = (TL::S - 1) * BK * 2;
-            auto period = [&](int kt, auto fast, auto slot) __attribute__((always_inline)) {
-                constexpr bool F = decltype(fast)::value;
-                const int se = slot;
-                const int s1 = wrap_slot<TL::S>(se + 1), s2 = wrap_slot<TL::S>(se + 2);
-                const int s4 = wrap_slot<TL::S>(se + TL::S - 1);
-                const char* cur = smem + se * TL::STAGE;
-                const char* nxt = smem + s1 * TL::STAGE;
-                const uint32_t st4 = ring + s4 * TL::STAGE, st5 = ring + se * TL::STAGE;
-                auto pairs = [&](int q, int t0) __attribute__((always_inline)) {
-                    if constexpr (F) {
-                        const int h = q & 1;
-                        cp.fast_a(t0 + (q >> 1), a4 + h * (BK * 2), h ? st5 : st4, wave);
-                    } else {
-                        a_pairs(cp, m0, q, t0, kt + TL::S - 1, s4, se);
-                    }
-                };
-                cm.template half<0, H>(cur, wm, wn, lane, [&](int q) __attribute__((always_inline)) {
-                    if constexpr (F)
-                        cp.fast_b(q, b4, st4, wave);
-                    else
-                        cp.issue_b(q, B, N, K, n0, (kt + TL::S - 1) * BK, st4, wave);
-                });
-                wait_vmcnt<TL::W0>();
-                __syncthreads();
-                if constexpr (PGEMM_POISON_LDS) {
-                    poison_stage<TL::STAGE, TL::T>(smem + se * TL::STAGE, opaque_tid());
-                    __syncthreads();
-                }
-                cm.template half<1, H>(nxt, wm, wn, lane,
-                                       [&](int q) __attribute__((always_inline)) { pairs(q, 0); });
-                cm.template half<2, H>(nxt, wm, wn, lane, [&](int q) __attribute__((always_inline)) {
-                    pairs(q, TL::A_CP / 2);
-                });
-                wait_vmcnt<TL::W1>();
-                __syncthreads();
-                if constexpr (PGEMM_POISON_LDS) {
-                    poison_stage<TL::STAGE, TL::T>(smem + s1 * TL::STAGE, opaque_tid());
-                    __syncthreads();
-                }
-                cm.template half<3, H>(smem + s2 * TL::STAGE, wm, wn, lane,
-                                       [&](int q) __attribute__((always_inline)) {
-                                           if constexpr (F)
-                                               cp.fast_b(q, b4 + bstep, st5, wave);
-                                           else
-                                               cp.issue_b(q, B, N, K, n0, (kt + TL::S) * BK,
-                                                          st5, wave);
-                                       });
-                b4 += 2 * bstep;
-                a4 += 2 * BK * 2;
-                return s2;
-            };
-            constexpr int S = TL::S;
-            const int fast_end = K / BK - S;
-            int kt = 0;
-            for (; kt + 2 * (S - 1) < fast_end && kt + 2 * (S - 1) < nk; kt += 2 * S)
-                ring_pass<S>(
-                    [&](auto j, auto slot) __attribute__((always_inline)) {
-                        period(kt + 2 * decltype(j)::value, std::true_type{}, slot);
-                    },
-                    std::make_integer_sequence<int, S>{});
-            cp.init(opaque_tid() & 63, wave, K, N, n0);
-            int se = 0;
-            for (; kt < fast_end && kt < nk; kt += 2) se = period(kt, std::true_type{}, se);
-            for (; kt < nk; kt += 2) se = period(kt, std::false_type{}, se);
-            wait_vmcnt<0>();
+            k_loop<TL>(
+                cm, cp, smem, ring, B, N, K, K, n0, nk, bstep, wm, wn, lane, wave,
+                [&](int q, int t0, int st, int sa, int sb) __attribute__((always_inline)) {
+                    a_pairs(cp, m0, q, t0, st, sa, sb);
+                },
+                [&]() __attribute__((always_inline)) { return opaque_tid() & 63; },
+                [&]() __attribute__((always_inline)) { return opaque_tid(); });
         }
         __syncthreads();  // every wave is done with the stage ring
         const int tid_d = opaque_tid();
