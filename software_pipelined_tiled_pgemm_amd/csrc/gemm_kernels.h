@@ -1081,8 +1081,7 @@ typedef const __attribute__((address_space(4))) PersistentArgs ConstPersistentAr
 // order, so all but the W0 youngest are done, step 0 among them.
 // Per-lane values are derived afresh in every tile (from an opaque copy of
 // the thread index), so none is kept live across the K loop beyond what
-// `kernel` keeps.  A separate kernel, so that the one-tile kernel's code is
-// unchanged.
+// `kernel` keeps.  The K loop itself is `kernel`'s (k_loop).
 template <class TL, int WPE>
 __global__ __launch_bounds__(TL::T, 1) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void kernel_persistent(const PersistentArgs) {
