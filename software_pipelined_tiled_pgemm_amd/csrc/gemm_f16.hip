@@ -3,6 +3,7 @@
 // gemm_f16_m16.hip.  The kernels are in gemm_kernels.h.
 
 #include <algorithm>
+#include <atomic>
 
 #include "gemm_kernels.h"
 
@@ -15,20 +16,33 @@ const TunedShape kTuned[] = {
 #include "gemm_tuned.inc"
 };
 
-double log2_ratio(int64_t a, int64_t b) {
-    const double x = log2((double)(a > 0 ? a : 1)) - log2((double)(b > 0 ? b : 1));
-    return x < 0 ? -x : x;
-}
+constexpr int kNumTuned = sizeof(kTuned) / sizeof(kTuned[0]);
+
+double log2_size(int64_t a) { return log2((double)(a > 0 ? a : 1)); }
+
+// log2 of every tuned M, N, K, computed once.
+struct TunedLogs {
+    double m[kNumTuned], n[kNumTuned], k[kNumTuned];
+    TunedLogs() {
+        for (int i = 0; i < kNumTuned; ++i) {
+            m[i] = log2_size(kTuned[i].M);
+            n[i] = log2_size(kTuned[i].N);
+            k[i] = log2_size(kTuned[i].K);
+        }
+    }
+};
 }  // namespace
 
 int gemm_choose_variant(int64_t M, int64_t N, int64_t K) {
+    static const TunedLogs logs;
+    const double lm = log2_size(M), ln = log2_size(N), lk = log2_size(K);
     int best = kGemm128x128;
     double best_d = 1e300;
-    for (const TunedShape& t : kTuned) {
-        const double d = log2_ratio(M, t.M) + log2_ratio(N, t.N) + log2_ratio(K, t.K);
+    for (int i = 0; i < kNumTuned; ++i) {
+        const double d = fabs(lm - logs.m[i]) + fabs(ln - logs.n[i]) + fabs(lk - logs.k[i]);
         if (d < best_d) {
             best_d = d;
-            best = t.variant;
+            best = kTuned[i].variant;
         }
     }
     return best;
@@ -76,11 +90,20 @@ hipError_t launch_variant(const void* A, const void* B, void* C, int64_t M, int6
 }  // namespace
 
 int compute_units() {
+    // Read once per device (the attribute query costs more host time than
+    // the rest of a small GEMM call's dispatch logic).
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
     int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         return 256;
+    if (dev >= 0 && dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 
