@@ -831,6 +831,67 @@ struct Compute<TL, 16> {
     }
 };
 
+// Copy schedule.  Step s lives in ring slot s mod S (S odd; 5 unless the
+// tile says otherwise).  The K loop runs in periods of two steps (kt even,
+// kt+1); a period issues the copies of steps kt+S-1 and kt+S (an even and
+// an odd step, so an A pair reads the two halves of the same 128-byte
+// lines), one operand per half-step, H copies each:
+//   step kt,   first half:  B of kt+S-1
+//   step kt,   second half: A pairs 0 .. A_CP/2-1 of (kt+S-1, kt+S)
+//   step kt+1, first half:  A pairs A_CP/2 .. A_CP-1 of (kt+S-1, kt+S)
+//   step kt+1, second half: B of kt+S
+// Slot of kt+S-1 (= slot of kt-1) is free after the barrier in the middle of
+// step kt-1, slot of kt+S (= slot of kt) after the one in the middle of step
+// kt, so every copy lands in a released slot.  The prologue issues steps
+// 0 .. S-2 in the same order.  The wait in the middle of step kt covers step
+// kt+1, issued as the second step of period kt+1-S: its last copy (B) is
+// followed by the (S-3)/2 periods between (4H copies each) and the first
+// half of period kt (H), so vmcnt <= W0 = H(2S-5).  The wait in the middle of
+// step kt+1 covers step kt+2, the first step of period kt+3-S: its last copy
+// (an A pair's first half) is followed by 1 + H + 4H(S-5)/2 + 3H copies, and
+// the kernel waits for vmcnt <= W1 = 2H(S-3), one more than needed.  After
+// the prologue, step 0's last copy is followed by 2H(S-1) - 3H + 1 copies:
+// the first wait is also W0.
+//
+// Copies of steps 0 .. S-2 of a tile into slots 0 .. S-2, in the order a
+// period issues them; with the steady-state copies when all of them lie
+// inside K.  `c` is the tile's copier (init and init_fast done); a_pairs as
+// for k_loop.
+template <class TL, class APairs>
+__device__ __forceinline__ void prologue(const Copier<TL>& c, const _Float16* B, int N, int K,
+                                         int n0, int64_t bstep, uint32_t ring, int wave,
+                                         APairs&& a_pairs) {
+    constexpr int H = TL::H;
+    if (K >= (TL::S - 1) * BK) {
+#pragma unroll
+        for (int e = 0; e < TL::S - 1; e += 2) {
+            const uint32_t ste = ring + e * TL::STAGE;
+#pragma unroll
+            for (int t = 0; t < H; ++t) c.fast_b(t, B + n0 + e * bstep, ste, wave);
+#pragma unroll
+            for (int q = 0; q < 2 * H; ++q) {
+                const int h = q & 1;
+                c.fast_a(q >> 1, (uint32_t)((e + h) * BK * 2), ste + h * TL::STAGE, wave);
+            }
+#pragma unroll
+            for (int t = 0; t < H; ++t)
+                c.fast_b(t, B + n0 + (e + 1) * bstep, ste + TL::STAGE, wave);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < TL::S - 1; e += 2) {
+#pragma unroll
+            for (int t = 0; t < H; ++t)
+                c.issue_b(t, B, N, K, n0, e * BK, ring + e * TL::STAGE, wave);
+#pragma unroll
+            for (int q = 0; q < 2 * H; ++q) a_pairs(q, 0, e, e, e + 1);
+#pragma unroll
+            for (int t = 0; t < H; ++t)
+                c.issue_b(t, B, N, K, n0, (e + 1) * BK, ring + (e + 1) * TL::STAGE, wave);
+        }
+    }
+}
+
 // The K loop of one tile: from the wait for step 0 (the prologue has issued
 // the copies of steps 0 .. S-2 into slots 0 .. S-2) to the end of the copies
 // past K.  a_pairs(q, t0, s, sa, sb): the general A copies of pair unit q,
@@ -936,28 +997,6 @@ __device__ __forceinline__ void k_loop(Compute<TL>& cm, Copier<TL>& cp, char* sm
     wait_vmcnt<0>();  // drain the copies of the steps past the end
 }
 
-// Copy schedule.  Step s lives in ring slot s mod S (S odd; 5 unless the
-// tile says otherwise).  The K loop runs in periods of two steps (kt even,
-// kt+1); a period issues the copies of steps kt+S-1 and kt+S (an even and
-// an odd step, so an A pair reads the two halves of the same 128-byte
-// lines), one operand per half-step, H copies each:
-//   step kt,   first half:  B of kt+S-1
-//   step kt,   second half: A pairs 0 .. A_CP/2-1 of (kt+S-1, kt+S)
-//   step kt+1, first half:  A pairs A_CP/2 .. A_CP-1 of (kt+S-1, kt+S)
-//   step kt+1, second half: B of kt+S
-// Slot of kt+S-1 (= slot of kt-1) is free after the barrier in the middle of
-// step kt-1, slot of kt+S (= slot of kt) after the one in the middle of step
-// kt, so every copy lands in a released slot.  The prologue issues steps
-// 0 .. S-2 in the same order.  The wait in the middle of step kt covers step
-// kt+1, issued as the second step of period kt+1-S: its last copy (B) is
-// followed by the (S-3)/2 periods between (4H copies each) and the first
-// half of period kt (H), so vmcnt <= W0 = H(2S-5).  The wait in the middle of
-// step kt+1 covers step kt+2, the first step of period kt+3-S: its last copy
-// (an A pair's first half) is followed by 1 + H + 4H(S-5)/2 + 3H copies, and
-// the kernel waits for vmcnt <= W1 = 2H(S-3), one more than needed.  After
-// the prologue, step 0's last copy is followed by 2H(S-1) - 3H + 1 copies:
-// the first wait is also W0.
-//
 // SPLIT (split-K): blockIdx.y = s takes the K chunk [s*chunk, s*chunk +
 // chunk) as a sub-matrix view (A shifted by s*chunk columns with its full row
 // pitch, B by s*chunk rows) and writes its fp32 partial product to
@@ -1000,38 +1039,9 @@ void kernel(const _Float16* __restrict__ A0, const _Float16* __restrict__ B0,
             const int t = t0 + (q >> 1), h = q & 1;
             cp.issue_a(t, A, M, K, m0, (s + h) * BK, ring + (h ? sb : sa) * TL::STAGE, wave);
         };
-        // Prologue: steps 0..S-2, in the order a period issues them; with the
-        // steady-state copies when all of them lie inside K.
         cp.init_fast(A, M, m0, N, n0);
         const int64_t bstep = (int64_t)BK * N;  // elements per B step
-        if (K >= (TL::S - 1) * BK) {
-#pragma unroll
-            for (int e = 0; e < TL::S - 1; e += 2) {
-                const uint32_t ste = ring + e * TL::STAGE;
-#pragma unroll
-                for (int t = 0; t < H; ++t) cp.fast_b(t, B + n0 + e * bstep, ste, wave);
-#pragma unroll
-                for (int q = 0; q < 2 * H; ++q) {
-                    const int h = q & 1;
-                    cp.fast_a(q >> 1, (uint32_t)((e + h) * BK * 2), ste + h * TL::STAGE, wave);
-                }
-#pragma unroll
-                for (int t = 0; t < H; ++t)
-                    cp.fast_b(t, B + n0 + (e + 1) * bstep, ste + TL::STAGE, wave);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < TL::S - 1; e += 2) {
-#pragma unroll
-                for (int t = 0; t < H; ++t)
-                    cp.issue_b(t, B, N, K, n0, e * BK, ring + e * TL::STAGE, wave);
-#pragma unroll
-                for (int q = 0; q < 2 * H; ++q) a_pairs(q, 0, e, e, e + 1);
-#pragma unroll
-                for (int t = 0; t < H; ++t)
-                    cp.issue_b(t, B, N, K, n0, (e + 1) * BK, ring + (e + 1) * TL::STAGE, wave);
-            }
-        }
+        prologue<TL>(cp, B, N, K, n0, bstep, ring, wave, a_pairs);
         k_loop<TL>(cm, cp, smem, ring, B, N, K, Kfull, n0, nk, bstep, wm, wn, lane, wave, a_pairs,
                    [&]() __attribute__((always_inline)) {
                        int l = lane;
@@ -1134,45 +1144,18 @@ void kernel_persistent(const PersistentArgs) {
             const int t = t0 + (q >> 1), h = q & 1;
             c.issue_a(t, A, M, K, pm0, (s + h) * BK, ring + (h ? sb : sa) * TL::STAGE, wave);
         };
-        // Steps 0..S-2 of the tile at (pm0, pn0) into slots 0..S-2, as in
-        // `kernel`.
-        auto prologue = [&](int pl, int pm0, int pn0) __attribute__((always_inline)) {
+        // Steps 0..S-2 of the tile at (pm0, pn0) into slots 0..S-2.
+        auto prologue_at = [&](int pl, int pm0, int pn0) __attribute__((always_inline)) {
             Copier<TL> c;
             c.init(pl, wave, K, N, pn0);
             c.init_fast(A, M, pm0, N, pn0);
-            if (K >= (TL::S - 1) * BK) {
-#pragma unroll
-                for (int e = 0; e < TL::S - 1; e += 2) {
-                    const uint32_t ste = ring + e * TL::STAGE;
-#pragma unroll
-                    for (int t = 0; t < H; ++t) c.fast_b(t, B + pn0 + e * bstep, ste, wave);
-#pragma unroll
-                    for (int q = 0; q < 2 * H; ++q) {
-                        const int h = q & 1;
-                        c.fast_a(q >> 1, (uint32_t)((e + h) * BK * 2), ste + h * TL::STAGE,
-                                 wave);
-                    }
-#pragma unroll
-                    for (int t = 0; t < H; ++t)
-                        c.fast_b(t, B + pn0 + (e + 1) * bstep, ste + TL::STAGE, wave);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < TL::S - 1; e += 2) {
-#pragma unroll
-                    for (int t = 0; t < H; ++t)
-                        c.issue_b(t, B, N, K, pn0, e * BK, ring + e * TL::STAGE, wave);
-#pragma unroll
-                    for (int q = 0; q < 2 * H; ++q) a_pairs(c, pm0, q, 0, e, e, e + 1);
-#pragma unroll
-                    for (int t = 0; t < H; ++t)
-                        c.issue_b(t, B, N, K, pn0, (e + 1) * BK, ring + (e + 1) * TL::STAGE,
-                                  wave);
-                }
-            }
+            prologue<TL>(c, B, N, K, pn0, bstep, ring, wave,
+                         [&](int q, int t0, int st, int sa, int sb) __attribute__((always_inline)) {
+                             a_pairs(c, pm0, q, t0, st, sa, sb);
+                         });
         };
 
-        if (first && nk > 0) prologue(lane, m0, n0);
+        if (first && nk > 0) prologue_at(lane, m0, n0);
         cm.zero();
         if (nk > 0) {
             Copier<TL> cp;
@@ -1198,7 +1181,7 @@ void kernel_persistent(const PersistentArgs) {
             tile_of_block(blk, ntiles, h->tiles_m, h->tiles_n, h->group_m, tm, tn);
             m0 = tm * TL::BM;
             n0 = tn * TL::BN;
-            if (nk > 0) prologue(tid_d & 63, m0, n0);
+            if (nk > 0) prologue_at(tid_d & 63, m0, n0);
         }
         cm.drain_bands(smem + (TL::S - 1) * TL::STAGE, h->C, M, N, dm0, dn0, tid_d, wm, wn);
         if (!more) break;
