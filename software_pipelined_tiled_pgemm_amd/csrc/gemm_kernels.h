@@ -1087,8 +1087,10 @@ typedef const __attribute__((address_space(4))) PersistentArgs ConstPersistentAr
 // through slot S-1 in bands of rows (drain_bands), so the next tile's
 // operands are in flight while this tile is converted and stored.  The next
 // tile's first wait (vmcnt <= W0) then also covers the drain's stores, which
-// were issued after those copies: vector memory operations complete in issue
-// order, so all but the W0 youngest are done, step 0 among them.
+// were issued after those copies: on gfx9 one counter (vmcnt) covers loads,
+// LDS-DMA loads and stores, which complete in issue order (the compiler's own
+// waits rely on the same), so all but the W0 youngest are done, step 0 among
+// them.
 // Per-lane values are derived afresh in every tile (from an opaque copy of
 // the thread index), so none is kept live across the K loop beyond what
 // `kernel` keeps.  The K loop itself is `kernel`'s (k_loop).
