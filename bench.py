@@ -309,18 +309,38 @@ def data_dependence(pg, inputs, stream, settle_s, steps, warmup):
 # ------------------------------------------------------------------ CPU baselines
 
 def _oracle_points_rate(oracle, A, B, I, J):
-    """(seconds, multiply-adds per second) of the oracle on sampled outputs."""
+    """(seconds, multiply-adds per second, (C, S)) of the oracle on sampled
+    outputs."""
     K = A.shape[1]
     t0 = time.perf_counter()
-    oracle.gemm_f16_points(A, B, I, J)
+    ref = oracle.gemm_f16_points(A, B, I, J)
     t = time.perf_counter() - t0
-    return t, I.size * K / t
+    return t, I.size * K / t, ref
 
 
-def cpu_baseline(inputs, target_seconds):
+def accuracy(workload, got, ref):
+    """The GPU's outputs `got` (fp16) against the oracle's correctly rounded
+    values and exact binary64 sums `ref` = (C, S) on the same outputs."""
+    import numpy as np
+    ref_c, ref_s = ref
+    g = got.astype(np.float64)
+    r = ref_c.astype(np.float64)
+    err = np.abs(g - r)
+    scaled = err / (np.abs(r) + 1.0)
+    return {"workload": workload, "outputs": int(got.size),
+            "max_abs_err": float(err.max()), "mean_abs_err": float(err.mean()),
+            "max_scaled_err": float(scaled.max()),
+            "frac_exact": round(float(np.mean(got.view(np.uint16) == ref_c.view(np.uint16))), 6),
+            "rel_frobenius_vs_exact_sums": float(np.linalg.norm(g - ref_s) / np.linalg.norm(ref_s)),
+            "tolerance": "|gpu - oracle| <= 5e-3 * (|oracle| + 1)",
+            "within_tolerance": bool(scaled.max() <= 5e-3)}
+
+
+def cpu_baseline(inputs, target_seconds, gpu_C=None):
     """The oracle (plain binary64 triple loop, all host threads) timed on a
     bounded sample of the headline workload: the first R full rows of the
-    4096^3 product, R chosen so the run takes about `target_seconds`."""
+    4096^3 product, R chosen so the run takes about `target_seconds`.
+    Returns (baseline, accuracy of gpu_C on those rows or None)."""
     import numpy as np
 
     import oracle
@@ -332,29 +352,35 @@ def cpu_baseline(inputs, target_seconds):
         I = np.repeat(np.arange(rows, dtype=np.int64), N)
         J = np.tile(np.arange(N, dtype=np.int64), rows)
         t0 = time.perf_counter()
-        oracle.gemm_f16_points(A, B, I, J)
-        return time.perf_counter() - t0
+        ref = oracle.gemm_f16_points(A, B, I, J)
+        return time.perf_counter() - t0, ref
 
     rows = 4
-    t = run(rows)
+    t, _ = run(rows)
     rows = int(max(4, min(M, rows * target_seconds / max(t, 1e-3))))
-    t = run(rows)
+    t, ref = run(rows)
     flops = 2.0 * rows * N * K
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": "first %d of 4096 rows of the 4096^3 fp16 GEMM (%.1f s, %d threads)"
-                      % (rows, t, cores)}
+    acc = None
+    if gpu_C is not None:
+        acc = accuracy("GEMM 4096^3 uniform (pgemm_f16), first %d rows" % rows,
+                       gpu_C[:rows].reshape(-1), ref)
+    return ({"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+             "sample": "first %d of 4096 rows of the 4096^3 fp16 GEMM (%.1f s, %d threads)"
+                       % (rows, t, cores)}, acc)
 
 
-def cpu_baselines_other(inputs):
+def cpu_baselines_other(inputs, gpu_out=None):
     """The oracle on the other configurations: 256^3 in full on one thread
     and on all threads; 8192^3 and 2048^2 x 32768 on the deterministic
     output sample the parity tests use (32 rows, 32 columns, 8192 points,
     the corners of every 128-tile), extrapolated to the whole product by the
     per-output time and labelled as such; the streaming add on the full
-    8192^2 workload on one thread and on all threads."""
+    8192^2 workload on one thread and on all threads.  Returns (baselines,
+    accuracy of the GPU outputs gpu_out[(M, N, K)] on those samples)."""
     import oracle
     allc = oracle.threads()
     out = []
+    accs = []
     A, B = inputs.gemm_inputs(256, 256, 256)
     for th in (1, allc):
         oracle.set_threads(th)
@@ -368,7 +394,10 @@ def cpu_baselines_other(inputs):
     for (M, N, K, dist) in [(8192, 8192, 8192, "normal"), (2048, 2048, 32768, "uniform")]:
         A, B = inputs.gemm_inputs(M, N, K, dist)
         I, J = inputs.sample_points(M, N, 8192)
-        t, rate = _oracle_points_rate(oracle, A, B, I, J)
+        t, rate, ref = _oracle_points_rate(oracle, A, B, I, J)
+        if gpu_out is not None and (M, N, K) in gpu_out:
+            accs.append(accuracy("GEMM %dx%dx%d %s (pgemm_f16), sampled outputs" % (M, N, K, dist),
+                                 gpu_out[(M, N, K)][I, J], ref))
         full = M * N * K / rate
         out.append({"workload": "GEMM %dx%dx%d %s" % (M, N, K, dist),
                     "value": 2.0 * rate / 1e12, "unit": "TFLOP/s", "cores": allc, "kind": "oracle",
@@ -390,7 +419,7 @@ def cpu_baselines_other(inputs):
         for k, v in list(r.items()):
             if isinstance(v, float):
                 r[k] = round(v, 6)
-    return out
+    return out, accs
 
 
 def main():
@@ -528,10 +557,20 @@ def main():
         out["fixed_cost"] = fixed_cost(pg, inputs, stream, settle_s)
         print("fixed cost: %s" % out["fixed_cost"]["fit_K_ge_512"], file=sys.stderr, flush=True)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(inputs, args.cpu_seconds)
-        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)
+        # The automatic path's outputs (one more untimed launch each) for the
+        # oracle leg's accuracy report.
+        gpu_out = {(4096, 4096, 4096): pg.pgemm_f16(head_ops[0], head_ops[1],
+                                                    C=head_ops[2]).cpu().numpy()}
         if not args.quick:
-            out["cpu_baseline_other"] = cpu_baselines_other(inputs)
+            for (M, N, Kk, dist, ops) in other_ops:
+                if M * N * Kk > 256 ** 3:
+                    gpu_out[(M, N, Kk)] = pg.pgemm_f16(ops[0], ops[1], C=ops[2]).cpu().numpy()
+        out["cpu_baseline"], acc = cpu_baseline(inputs, args.cpu_seconds, gpu_out[(4096, 4096, 4096)])
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)
+        out["accuracy"] = [acc]
+        if not args.quick:
+            out["cpu_baseline_other"], accs = cpu_baselines_other(inputs, gpu_out)
+            out["accuracy"] += accs
     print(json.dumps(out), flush=True)
 
 
