@@ -46,6 +46,13 @@ DEFAULT_SHAPES = [
     (2048, 8192, 2048), (8192, 2048, 8192), (6144, 2048, 4096), (2048, 6144, 4096),
     (12288, 12288, 4096), (16384, 16384, 1024),
 ]
+# Plus a grid in log space, so that the nearest tuned shape of a new problem
+# is never far off: M, N in 512 .. 16384 and K in 256 .. 16384 (products up
+# to 2^41 flop/2).
+GRID_MN = (512, 1024, 2048, 4096, 8192, 16384)
+GRID_K = (256, 1024, 4096, 16384)
+DEFAULT_SHAPES += [(m, n, k) for m in GRID_MN for n in GRID_MN for k in GRID_K
+                   if m * n * k <= 1 << 41 and (m, n, k) not in DEFAULT_SHAPES]
 
 _ENTRY = re.compile(r"^\{\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)\s*\},")
 
@@ -71,15 +78,19 @@ def measure(shapes=None, variants=None, rounds=3, target_s=0.02, log=None):
     {"M", "N", "K", "tflops": {variant: best TFLOP/s}}."""
     import torch
 
-    from . import inputs, lib
+    from . import lib
     L = lib()
     shapes = list(shapes or DEFAULT_SHAPES)
     variants = list(variants or range(1, L.pgemm_f16_num_variants() + 1))
     stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
     out = []
     for (M, N, K) in shapes:
-        A, B = inputs.gemm_inputs(M, N, K, "uniform")
-        tA, tB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        # U[-1, 1] operands, drawn on the device (the timing depends on the
+        # distribution, which sets the power draw, not on the exact values)
+        tA = (torch.rand((M, K), generator=gen, device="cuda") * 2 - 1).half()
+        tB = (torch.rand((K, N), generator=gen, device="cuda") * 2 - 1).half()
         tC = torch.empty((M, N), dtype=torch.float16, device="cuda")
         ptrs = (tA.data_ptr(), tB.data_ptr(), tC.data_ptr())
         # launches per batch: about target_s of GPU time per variant
