@@ -47,10 +47,10 @@ DEFAULT_SHAPES = [
     (12288, 12288, 4096), (16384, 16384, 1024),
 ]
 # Plus a grid in log space, so that the nearest tuned shape of a new problem
-# is never far off: M, N in 512 .. 16384 and K in 256 .. 16384 (products up
+# is never far off: M, N in 256 .. 16384 and K in 256 .. 32768 (products up
 # to 2^41 flop/2).
-GRID_MN = (512, 1024, 2048, 4096, 8192, 16384)
-GRID_K = (256, 1024, 4096, 16384)
+GRID_MN = (256, 512, 1024, 2048, 4096, 8192, 16384)
+GRID_K = (256, 1024, 4096, 16384, 32768)
 DEFAULT_SHAPES += [(m, n, k) for m in GRID_MN for n in GRID_MN for k in GRID_K
                    if m * n * k <= 1 << 41 and (m, n, k) not in DEFAULT_SHAPES]
 
