@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--data-dependence", action="store_true",
                     help="also time the 4096^3 and 8192^3 GEMMs on U[-1,1], normal(0,1/sqrt(K)) "
                          "and all-zero operands (same instructions, different switching power)")
+    ap.add_argument("--zero-operands", action="store_true",
+                    help="diagnostic: the 4096^3 legs on all-zero operands (same instructions, "
+                         "no operand switching); the line then names them and is not the headline")
     ap.add_argument("--fixed-cost", action="store_true",
                     help="also time the 256x256-tile GEMM at M=N=4096 for K = 0 .. 4096 and fit "
                          "time = fixed + steps * per_step (the per-launch cost outside the K loop)")
@@ -453,6 +456,9 @@ def main():
 
     # Every input on the device before the first timed leg.
     head_ops = gemm_operands(inputs, 4096, 4096, 4096, "uniform")
+    if args.zero_operands:  # diagnostic only: no oracle leg on these operands
+        head_ops = (torch.zeros_like(head_ops[0]), torch.zeros_like(head_ops[1]), head_ops[2])
+        args.no_cpu = True
     if not args.quick:
         x, y = inputs.stream_inputs((8192, 8192))
         sets = [(torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda(),
@@ -534,8 +540,9 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": "fp16 GEMM M=N=K=4096, row-major A and B, U[-1,1] inputs, "
-                               "fp32 accumulate, fp16 out"},
+        "config": {"workload": "fp16 GEMM M=N=K=4096, row-major A and B, %s inputs, "
+                               "fp32 accumulate, fp16 out"
+                               % ("ALL-ZERO (diagnostic)" if args.zero_operands else "U[-1,1]")},
         "roofline": {"bound": "mfma", "achieved": round(head["tflops"], 2),
                      "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(head["frac_of_peak"], 4), "traffic": traffic},
