@@ -87,6 +87,20 @@ def _check_dev(t, dtype, name, ndim=None):
         raise ValueError("%s must be contiguous (row-major)" % name)
 
 
+def _new(shape, dtype, device, stream):
+    """An empty tensor for a call on `stream` (None: the current stream).
+    torch's caching allocator keeps one pool per stream and orders reuse by
+    that stream alone, so memory for a call on another stream is taken from
+    that stream's pool: a block from the current stream's pool could still
+    be in use by pending work there, and would go back to that pool, free for
+    the current stream, while the call's kernels still use it."""
+    torch = _torch()
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _call(rc, what):
     if rc != PGEMM_OK:
         raise PgemmError(rc, what)
@@ -110,7 +124,7 @@ def pgemm_f16_variant(A, B, variant, C=None, stream=None):
     if K != K2:
         raise ValueError("inner dimensions differ: %s @ %s" % (tuple(A.shape), tuple(B.shape)))
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+        C = _new((M, N), torch.float16, A.device, stream)
     else:
         _check_dev(C, torch.float16, "C", 2)
         if C.shape != (M, N) or C.get_device() != dev_a:
@@ -148,7 +162,7 @@ def pgemm_f16_splitk(A, B, splits=None, C=None, workspace=None, stream=None):
     if K != K2 or A.device != B.device:
         raise ValueError("inner dimensions or devices differ")
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+        C = _new((M, N), torch.float16, A.device, stream)
     else:
         _check_dev(C, torch.float16, "C", 2)
         if tuple(C.shape) != (M, N) or C.device != A.device:
@@ -157,7 +171,7 @@ def pgemm_f16_splitk(A, B, splits=None, C=None, workspace=None, stream=None):
         splits = pgemm_f16_splitk_default_splits(M, N, K)
     need = pgemm_f16_splitk_workspace_bytes(M, N, K, splits)
     if workspace is None:
-        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=A.device)
+        workspace = _new(max(need // 4, 1), torch.float32, A.device, stream)
     elif workspace.device != A.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on %s" % A.device)
     f = lib().pgemm_f16_splitk
@@ -181,7 +195,7 @@ def pgemm_f16_splitk_noalloc(A, B, splits=None, C=None, stream=None):
     if K != K2 or A.get_device() != B.get_device():
         raise ValueError("inner dimensions or devices differ")
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+        C = _new((M, N), torch.float16, A.device, stream)
     else:
         _check_dev(C, torch.float16, "C", 2)
         if C.shape != (M, N) or C.get_device() != A.get_device():
@@ -220,10 +234,10 @@ def pgemm_f16_plan(M, N, K, cus=0):
     return head.value, hv.value, tv.value
 
 
-def _elementwise_out(x, z):
+def _elementwise_out(x, z, stream):
     torch = _torch()
     if z is None:
-        return torch.empty_like(x)
+        return _new(tuple(x.shape), torch.float32, x.device, stream)
     _check_dev(z, torch.float32, "z")
     if z.numel() != x.numel() or z.get_device() != x.get_device():
         raise ValueError("z must have x's size and device")
@@ -242,7 +256,7 @@ def pstream_add_blocked(x, y, block_elems, z=None, stream=None):
     _check_dev(y, torch.float32, "y")
     if x.numel() != y.numel() or x.get_device() != y.get_device():
         raise ValueError("x and y must have the same size and device")
-    z = _elementwise_out(x, z)
+    z = _elementwise_out(x, z, stream)
     L = lib()
     if block_elems is None:
         rc = _invoke(x, stream, lambda h: L.pstream_add(x.data_ptr(), y.data_ptr(), z.data_ptr(),
@@ -258,7 +272,7 @@ def pstream_add_scalar(x, c, z=None, stream=None):
     """z = x + c elementwise (fp32); z may be x (in place)."""
     torch = _torch()
     _check_dev(x, torch.float32, "x")
-    z = _elementwise_out(x, z)
+    z = _elementwise_out(x, z, stream)
     f = lib().pstream_add_scalar
     rc = _invoke(x, stream, lambda h: f(x.data_ptr(), float(c), z.data_ptr(), x.numel(), h))
     _call(rc, "pstream_add_scalar")
@@ -274,7 +288,7 @@ def preduce_sum_f32(x, out=None, stream=None):
         raise ValueError("x needs at least one dimension")
     R = x.shape[0]
     if out is None:
-        out = torch.empty(tuple(x.shape[1:]), dtype=torch.float32, device=x.device)
+        out = _new(tuple(x.shape[1:]), torch.float32, x.device, stream)
     else:
         _check_dev(out, torch.float32, "out")
         if tuple(out.shape) != tuple(x.shape[1:]) or out.device != x.device:
@@ -287,7 +301,7 @@ def preduce_sum_f32(x, out=None, stream=None):
 
 def pgemm_test_fill_f32(n, v=42.0, device="cuda", out=None, stream=None):
     torch = _torch()
-    o = out if out is not None else torch.empty(int(n), dtype=torch.float32, device=device)
+    o = out if out is not None else _new(int(n), torch.float32, device, stream)
     _check_dev(o, torch.float32, "out")
     f = lib().pgemm_test_fill_f32
     rc = _invoke(o, stream, lambda h: f(o.data_ptr(), float(v), o.numel(), h))
@@ -297,7 +311,7 @@ def pgemm_test_fill_f32(n, v=42.0, device="cuda", out=None, stream=None):
 
 def pgemm_test_iota_f32(n, device="cuda", out=None, stream=None):
     torch = _torch()
-    o = out if out is not None else torch.empty(int(n), dtype=torch.float32, device=device)
+    o = out if out is not None else _new(int(n), torch.float32, device, stream)
     _check_dev(o, torch.float32, "out")
     f = lib().pgemm_test_iota_f32
     rc = _invoke(o, stream, lambda h: f(o.data_ptr(), o.numel(), h))

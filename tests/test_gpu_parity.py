@@ -715,6 +715,32 @@ def test_gemm_splitk_full_size_sampled():
     assert_fp32_bound(got[I, J], ref, Sabs, K, "split-K long K")
 
 
+def test_gemm_splitk_on_a_side_stream_keeps_its_workspace():
+    # The binding allocates the split-K workspace and C for a call with
+    # stream=side. That memory must not be free for the current stream while
+    # the side stream still runs the call: blocks of the workspace's size,
+    # taken and filled with NaN on the current stream over the whole call,
+    # must never be the workspace (or C).
+    M, N, K = 2048, 2048, 32768
+    say("gemm split-K on a side stream %dx%dx%d" % (M, N, K))
+    A, B = inputs.gemm_inputs(M, N, K, seed_a=61, seed_b=62)
+    tA, tB = dev(A), dev(B)
+    ref = host(pg.pgemm_f16_splitk(tA, tB, 4))
+    need = pg.pgemm_f16_splitk_workspace_bytes(M, N, K, 4)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(4):
+        outs.append(pg.pgemm_f16_splitk(tA, tB, 4, stream=side))
+        for _ in range(24):  # about 24 x 15 us, longer than the call
+            junk = torch.empty(need // 4, dtype=torch.float32, device="cuda:0")
+            junk.fill_(float("nan"))
+            del junk
+    torch.cuda.synchronize()
+    for i, C in enumerate(outs):
+        assert bits_equal(C.cpu().numpy(), ref), "side-stream call %d differs" % i
+
+
 def test_gemm_splitk_device_argument_checks():
     L = pg.lib()
     buf = torch.zeros(1 << 20, dtype=torch.float16, device="cuda:0")
