@@ -94,8 +94,11 @@ int pgemm_f16(const void* A, const void* B, void* C,
  *   9  as 8, persistent: at most one workgroup per compute unit, each
  *      walking several output tiles; the copies of a tile's first steps
  *      are issued before the previous tile's output is stored
+ *   10 as 7 with a ring of 7 stages (copies up to 6 steps ahead; the
+ *      quickstart's max_concurrent_steps), one workgroup per compute unit
+ *   11 as 7 with a ring of 9 stages (copies up to 8 steps ahead)
  * Variants 1-6 give bit-identical results for the same inputs, and so do
- * variants 7-9: inside a family the grouping of the K sum of each output
+ * variants 7-11: inside a family the grouping of the K sum of each output
  * element depends neither on the tiling nor on the pipeline.  The two
  * families group the products differently (16 vs 32 per instruction), so
  * they may differ in the last bits; both are within the accuracy bound.

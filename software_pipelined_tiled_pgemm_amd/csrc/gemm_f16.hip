@@ -69,6 +69,8 @@ hipError_t launch_variant(const void* A, const void* B, void* C, int64_t M, int6
         case kGemm128x128m16:
         case kGemm256x256w8m16:
         case kGemm256x256w8m16p:
+        case kGemm128x128m16s7:
+        case kGemm128x128m16s9:
             return launch_gemm_f16_m16(A, B, C, M, N, K, variant, stream);
         case kGemmWs128x128: {
             using TL = dm::Tile<128, 128>;

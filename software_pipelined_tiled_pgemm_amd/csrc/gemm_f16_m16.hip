@@ -1,4 +1,4 @@
-// fp16 GEMM entry points of the 16x16x32 family (variants 7, 8, 9) and the
+// fp16 GEMM entry points of the 16x16x32 family (variants 7-11) and the
 // split-K path, which runs on the same kernels.
 //
 // This file is compiled with MFMA results kept in ordinary VGPRs (no
@@ -28,6 +28,14 @@ hipError_t launch_gemm_f16_m16(const void* A, const void* B, void* C, int64_t M,
             using TL = dm::Tile<256, 256, 2, 4, 16>;
             return launch_persistent<TL>(dm::kernel_persistent<TL, 2>, TL::T, A, B, C, M, N, K,
                                          compute_units(), stream);
+        }
+        case kGemm128x128m16s7: {
+            using TL = dm::Tile<128, 128, 2, 2, 16, 7>;
+            return launch<TL>(dm::kernel<TL, 1>, TL::T, 1, A, B, C, M, N, K, stream, nows, 0);
+        }
+        case kGemm128x128m16s9: {
+            using TL = dm::Tile<128, 128, 2, 2, 16, 9>;
+            return launch<TL>(dm::kernel<TL, 1>, TL::T, 1, A, B, C, M, N, K, stream, nows, 0);
         }
         default:
             return hipErrorInvalidValue;

@@ -25,7 +25,12 @@ enum GemmVariant : int {
     // tiles, the next tile's first copies overlapping this tile's drain.
     // Bit-identical to variants 7 and 8 (the same K order).
     kGemm256x256w8m16p = 9,
-    kGemmNumVariants = 9,
+    // Variant 7 with a deeper ring (the pages' max_concurrent_steps knob): 7
+    // or 9 LDS stages (112 or 144 KiB, so one workgroup per CU), copies up
+    // to 6 or 8 steps ahead.  Bit-identical to variants 7-9.
+    kGemm128x128m16s7 = 10,
+    kGemm128x128m16s9 = 11,
+    kGemmNumVariants = 11,
 };
 
 // Picks a concrete variant for a problem shape: the variant measured fastest

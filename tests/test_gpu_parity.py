@@ -87,10 +87,10 @@ def bits_equal(a, b):
     return np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-VARIANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9]
+VARIANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11]
 # Variants that must agree bit for bit: the same matrix instruction, so the
-# same grouping of each output's K sum (32x32x16: 1-6; 16x16x32: 7-9).
-FAMILIES = [[1, 2, 3, 4, 5, 6], [7, 8, 9]]
+# same grouping of each output's K sum (32x32x16: 1-6; 16x16x32: 7-11).
+FAMILIES = [[1, 2, 3, 4, 5, 6], [7, 8, 9, 10, 11]]
 
 
 # ------------------------------------------------------------ worked examples
