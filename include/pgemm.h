@@ -172,24 +172,32 @@ int pgemm_f16_splitk_default_splits(int64_t M, int64_t N, int64_t K);
 
 /*
  * The variant (1 .. pgemm_f16_num_variants()) that pgemm_f16 uses for an
- * M x N x K problem: the fastest variant on the nearest shape of the tuned
- * table built into the library.  The table is written by the autotuner
- * (software_pipelined_tiled_pgemm_amd/autotune.py), which times every
- * variant -- tile shape, pipeline depth and wave count -- on a set of
- * shapes; the pages name block size as the main tuning knob (software
- * pipelining guide, section 6.1) and advise autotuning the number of
- * concurrent copies (Chinese quickstart, section on emit_pipeline's key
- * parameters).  Nearest means the smallest sum of |log2| ratios over M, N
- * and K.  Pure host function: no HIP call, no device needed.
- * Returns PGEMM_EINVAL for a negative size.
+ * M x N x K problem on the current device.  The tuned table built into the
+ * library holds every variant's measured TFLOP/s on a set of shapes; it is
+ * written by the autotuner (software_pipelined_tiled_pgemm_amd/autotune.py),
+ * which times every variant -- tile shape, pipeline depth and wave count;
+ * the pages name block size as the main tuning knob (software pipelining
+ * guide, section 6.1) and advise autotuning the number of concurrent copies
+ * (Chinese quickstart, section on emit_pipeline's key parameters).  The
+ * choice is the fastest variant of the tuned shape T nearest to the problem
+ * (smallest sum of |log2| ratios over M, N and K), unless the tile count of
+ * the problem fills the CUs far worse than T's: each variant's rate on T is
+ * scaled by fill(M, N) / fill(T.M, T.N), fill being M*N / (waves * slots *
+ * tile area) with slots = (workgroups per CU) * CUs and waves =
+ * ceil(tiles / slots) for the variant's 256x256 or 128x128 tile, and the
+ * best estimate (the lowest id within 1% of it) replaces T's variant if it
+ * beats that variant's estimate by more than 30%.  Host
+ * function: its only HIP calls read the current device's CU count, once per
+ * device (256 when there is no device).  Returns PGEMM_EINVAL for a
+ * negative size.
  */
 int pgemm_f16_choose_variant(int64_t M, int64_t N, int64_t K);
 
 /*
  * The launches pgemm_f16 makes for an M x N x K problem on a device with
  * `cus` compute units (cus <= 0: the current device's count, 256 if it
- * cannot be read).  Usually one: pgemm_f16_choose_variant's variant over all
- * M rows (*head_rows = M, *tail_variant = 0).  When that variant uses
+ * cannot be read).  Usually one: the variant pgemm_f16_choose_variant picks
+ * on such a device, over all M rows (*head_rows = M, *tail_variant = 0).  When that variant uses
  * 256x256 tiles and their last wave over the CUs would be mostly idle, the
  * first *head_rows rows (a multiple of 256) run with it and the remaining
  * M - *head_rows rows with *tail_variant, the 128x128 variant of the same

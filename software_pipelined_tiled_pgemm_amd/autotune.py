@@ -7,9 +7,12 @@ key parameters).  Here the knobs are bundled into the variants of
 pgemm_f16_variant (output tile 256x256 or 128x128, LDS-DMA ring of 5 stages
 or register-staged 2 stages, 4 or 8 waves, 32x32x16 or 16x16x32 matrix
 instruction).  This module times every variant
-on a set of shapes and writes the shape -> fastest-variant table that is
-compiled into libpgemm (csrc/gemm_tuned.inc); pgemm_f16 (variant 0) then
-runs the variant of the tuned shape nearest to the problem.
+on a set of shapes and writes the table of every variant's rate per shape
+that is compiled into libpgemm (csrc/gemm_tuned.inc).  pgemm_f16 (variant
+0) then runs the fastest variant of the tuned shape nearest to the
+problem, unless scaling every variant's rate there by how well its tiles
+fill the CUs on the problem against on the tuned shape predicts another
+variant more than 30% faster (choose() restates the library's rule).
 
 Timing: each variant launches back to back on one stream with HIP events
 around the batch; the variants of a shape are interleaved over several
@@ -54,7 +57,7 @@ GRID_K = (256, 1024, 4096, 16384, 32768)
 DEFAULT_SHAPES += [(m, n, k) for m in GRID_MN for n in GRID_MN for k in GRID_K
                    if m * n * k <= 1 << 41 and (m, n, k) not in DEFAULT_SHAPES]
 
-_ENTRY = re.compile(r"^\{\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)\s*\},")
+_ENTRY = re.compile(r"^\{\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+)\s*,\s*\{([^}]*)\}\s*\},")
 
 
 def _time_batch(lib, ptrs, M, N, K, variant, n, stream):
@@ -125,31 +128,87 @@ def fastest(rec) -> int:
 
 
 def render_table(records, device: str = "") -> str:
+    """The table as C initialisers {M, N, K, fastest, {rate of v1, v2, ...}}.
+    Rates are rounded to 0.1 TFLOP/s first; the fastest variant is taken
+    from the rounded rates, which are what the library reads."""
     lines = ["// Generated by software_pipelined_tiled_pgemm_amd/autotune.py; do not edit.",
-             "// {M, N, K, fastest variant},  // best TFLOP/s of each variant"]
+             "// {M, N, K, fastest variant, {best TFLOP/s of variant 1, 2, ...}},"]
     if device:
         lines.append("// Measured on %s." % device)
     for r in records:
-        perf = " ".join("v%d %.1f" % (v, x) for v, x in sorted(r["tflops"].items()))
-        lines.append("{%d, %d, %d, %d},  // %s" % (r["M"], r["N"], r["K"], fastest(r), perf))
+        rates = {v: round(x, 1) for v, x in r["tflops"].items()}
+        nv = max(rates)
+        vals = ", ".join("%.1f" % rates.get(v, 0.0) for v in range(1, nv + 1))
+        lines.append("{%d, %d, %d, %d, {%s}}," % (r["M"], r["N"], r["K"],
+                                                 fastest({"tflops": rates}), vals))
     return "\n".join(lines) + "\n"
 
 
+def parse_rates(text: str):
+    """(M, N, K, fastest variant, {variant: TFLOP/s}) entries of a table."""
+    out = []
+    for m in map(_ENTRY.match, text.splitlines()):
+        if m:
+            M, N, K, v = (int(g) for g in m.groups()[:4])
+            rates = {i + 1: float(x) for i, x in enumerate(m.group(5).split(","))}
+            out.append((M, N, K, v, rates))
+    return out
+
+
 def parse_table(text: str):
-    """(M, N, K, variant) entries of a generated table."""
-    return [tuple(int(g) for g in m.groups()) for m in map(_ENTRY.match, text.splitlines()) if m]
+    """(M, N, K, fastest variant) entries of a generated table."""
+    return [e[:4] for e in parse_rates(text)]
 
 
-def nearest(table, M, N, K) -> int:
-    """The choice rule the library applies to a table (reference for tests)."""
-    def lr(a, b):
-        return abs(math.log2(max(a, 1)) - math.log2(max(b, 1)))
-    best, best_d = 2, float("inf")
-    for (tm, tn, tk, v) in table:
-        d = lr(M, tm) + lr(N, tn) + lr(K, tk)
-        if d < best_d:
-            best, best_d = v, d
-    return best
+# Tile edge of each variant of pgemm_f16_variant (the others use 128x128),
+# and the variants of which two workgroups fit on one CU (the others: one).
+TILE_256 = (1, 3, 5, 8, 9)
+TWO_PER_CU = (2, 4, 6, 7)
+# The choice leaves the nearest tuned shape's fastest variant only for an
+# estimate more than this much faster.
+REFILL_GAIN = 1.3
+
+
+def slot_fill(M, N, b, slots):
+    """Useful share of the workgroup slots of an M x N launch with b x b
+    tiles: M*N / (waves * slots * b*b), waves = ceil(tiles / slots)."""
+    tiles = ((M + b - 1) // b) * ((N + b - 1) // b)
+    waves = (tiles + slots - 1) // slots
+    return float(M) * float(N) / (float(waves) * slots * b * b)
+
+
+def choose(rates_table, M, N, K, cus=256, num_variants=None) -> int:
+    """The library's choice for an M x N x K problem on `cus` CUs, from
+    parse_rates() entries (restated here for the tests): the nearest tuned
+    shape T (sum of |log2| ratios over M, N, K; the first on ties) and its
+    fastest variant v0; each variant's rate on T scaled by slot_fill on the
+    problem over slot_fill on T; the best estimate (lowest id within TIE)
+    replaces v0 only if it beats v0's estimate by more than REFILL_GAIN."""
+    if not rates_table or M <= 0 or N <= 0:
+        return 2
+    if cus <= 0:
+        cus = 256
+
+    def l2(a):
+        return math.log2(max(a, 1))
+    lm, ln, lk = l2(M), l2(N), l2(K)
+    near, near_d = None, float("inf")
+    for e in rates_table:
+        d = abs(lm - l2(e[0])) + abs(ln - l2(e[1])) + abs(lk - l2(e[2]))
+        if d < near_d:
+            near, near_d = e, d
+    tm, tn, _, v0, rates = near
+    nv = num_variants or max(rates)
+    est = {}
+    for v in range(1, nv + 1):
+        b = 256 if v in TILE_256 else 128
+        slots = (2 if v in TWO_PER_CU else 1) * cus
+        est[v] = rates.get(v, 0.0) * slot_fill(M, N, b, slots) / slot_fill(tm, tn, b, slots)
+    top = max(est.values())
+    if not 1 <= v0 <= nv or top <= 0.0:
+        return 2
+    alt = min(v for v in est if est[v] >= (1.0 - TIE) * top)
+    return alt if est[alt] > REFILL_GAIN * est[v0] else v0
 
 
 def main(argv=None):

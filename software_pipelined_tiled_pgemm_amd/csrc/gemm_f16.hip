@@ -33,19 +33,72 @@ struct TunedLogs {
 };
 }  // namespace
 
-int gemm_choose_variant(int64_t M, int64_t N, int64_t K) {
+// Output tile edge of a variant (256 or 128).
+int variant_tile(int v) {
+    switch (v) {
+        case kGemm256x256:
+        case kGemmRs256x256:
+        case kGemm256x256w8:
+        case kGemm256x256w8m16:
+        case kGemm256x256w8m16p:
+            return 256;
+        default:
+            return 128;
+    }
+}
+
+// Workgroups of a variant that fit on one CU at once (LDS-bound).
+int variant_wgs_per_cu(int v) {
+    switch (v) {
+        case kGemm128x128:
+        case kGemmRs128x128:
+        case kGemmWs128x128:
+        case kGemm128x128m16:
+            return 2;
+        default:
+            return 1;
+    }
+}
+
+// Useful share of the slots an M x N launch of tile edge b occupies, with
+// `slots` workgroups resident at once: M*N / (waves * slots * b*b),
+// waves = ceil(tiles / slots).
+double slot_fill(int64_t M, int64_t N, int b, int64_t slots) {
+    const int64_t tiles = ((M + b - 1) / b) * ((N + b - 1) / b);
+    const int64_t waves = (tiles + slots - 1) / slots;
+    return (double)M * (double)N / ((double)waves * slots * b * b);
+}
+
+int gemm_choose_variant(int64_t M, int64_t N, int64_t K, int cus) {
     static const TunedLogs logs;
+    if (kNumTuned == 0) return kGemm128x128;
+    if (cus <= 0) cus = 256;
+    if (M <= 0 || N <= 0) return kGemm128x128;
     const double lm = log2_size(M), ln = log2_size(N), lk = log2_size(K);
-    int best = kGemm128x128;
-    double best_d = 1e300;
+    int near = 0;
+    double near_d = 1e300;
     for (int i = 0; i < kNumTuned; ++i) {
         const double d = fabs(lm - logs.m[i]) + fabs(ln - logs.n[i]) + fabs(lk - logs.k[i]);
-        if (d < best_d) {
-            best_d = d;
-            best = kTuned[i].variant;
+        if (d < near_d) {
+            near_d = d;
+            near = i;
         }
     }
-    return best;
+    const TunedShape& t = kTuned[near];
+    const int v0 = t.variant;
+    double est[kGemmNumVariants];
+    double top = 0.0;
+    for (int v = 1; v <= kGemmNumVariants; ++v) {
+        const int b = variant_tile(v);
+        const int64_t slots = (int64_t)variant_wgs_per_cu(v) * cus;
+        est[v - 1] = t.tflops[v - 1] * slot_fill(M, N, b, slots) / slot_fill(t.M, t.N, b, slots);
+        top = std::max(top, est[v - 1]);
+    }
+    if (v0 < 1 || v0 > kGemmNumVariants || top <= 0.0) return kGemm128x128;
+    int alt = v0;
+    for (int v = kGemmNumVariants; v >= 1; --v)
+        if (est[v - 1] >= (1.0 - 0.01) * top) alt = v;
+    return est[alt - 1] > kRefillGain * est[v0 - 1] ? alt : v0;
 }
 
 namespace {
@@ -147,8 +200,9 @@ int64_t gemm_head_rows(int64_t M, int64_t N, int64_t K, int variant, int cus) {
 hipError_t launch_gemm_f16(const void* A, const void* B, void* C, int64_t M, int64_t N,
                            int64_t K, int variant, hipStream_t stream) {
     if (variant != kGemmAuto) return launch_variant(A, B, C, M, N, K, variant, stream);
-    variant = gemm_choose_variant(M, N, K);
-    const int64_t head = gemm_head_rows(M, N, K, variant, compute_units());
+    const int cus = compute_units();
+    variant = gemm_choose_variant(M, N, K, cus);
+    const int64_t head = gemm_head_rows(M, N, K, variant, cus);
     if (head >= M) return launch_variant(A, B, C, M, N, K, variant, stream);
     // Head rows on the 256x256 tile, the rest on the 128x128 tile of the
     // same matrix-instruction family: every output's K sum is grouped the

@@ -33,14 +33,28 @@ enum GemmVariant : int {
     kGemmNumVariants = 11,
 };
 
-// Picks a concrete variant for a problem shape: the variant measured fastest
-// on the tuned shape nearest to (M, N, K) (gemm_tuned.inc, written by the
-// autotuner), distance = sum over M, N, K of |log2(shape / tuned shape)|.
-int gemm_choose_variant(int64_t M, int64_t N, int64_t K);
+// Picks a concrete variant for a problem shape on a device with `cus` CUs.
+// The tuned table (gemm_tuned.inc, written by the autotuner) holds, for each
+// tuned shape, the fastest variant and every variant's measured TFLOP/s.
+// Take the tuned shape T nearest to (M, N, K) (distance = sum over M, N, K
+// of |log2(shape / T)|) and its fastest variant v0.  Estimate each
+// variant's rate on (M, N, K) as its rate on T times fill(M, N) / fill(T),
+// fill being the useful share of the workgroup slots the launch occupies:
+// M*N / (waves * slots * tile area), slots = workgroups per CU * cus,
+// waves = ceil(tiles / slots).  Let alt be the fastest estimate (the lowest
+// id within 1% of it): the choice is alt if its estimate beats v0's by more
+// than kRefillGain, else v0.  So the nearest tuned shape decides unless the
+// problem's tile count lands far worse on the CUs than T's for v0 (a shape
+// just past a multiple of the tile, or with far fewer tiles).
+int gemm_choose_variant(int64_t M, int64_t N, int64_t K, int cus);
+// Measured on 240 random shapes against the nearest-shape rule alone: a
+// smaller margin changes more choices for the worse than for the better.
+constexpr double kRefillGain = 1.3;
 
 struct TunedShape {
     int64_t M, N, K;
-    int variant;
+    int variant;                      // fastest on this shape (informative)
+    double tflops[kGemmNumVariants];  // measured rate of variant v at [v - 1]
 };
 
 // Variant kGemmAuto runs gemm_choose_variant's pick, except that when its

@@ -156,15 +156,16 @@ int pgemm_f16_splitk_noalloc(const void* A, const void* B, void* C, int64_t M, i
 
 int pgemm_f16_choose_variant(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return PGEMM_EINVAL;
-    return pgemm::gemm_choose_variant(M, N, K);
+    return pgemm::gemm_choose_variant(M, N, K, pgemm::compute_units());
 }
 
 int pgemm_f16_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* head_rows,
                    int* head_variant, int* tail_variant) {
     if (M < 0 || N < 0 || K < 0 || !head_rows || !head_variant || !tail_variant)
         return PGEMM_EINVAL;
-    const int v = pgemm::gemm_choose_variant(M, N, K);
-    const int64_t head = pgemm::gemm_head_rows(M, N, K, v, cus > 0 ? cus : pgemm::compute_units());
+    const int c = cus > 0 ? cus : pgemm::compute_units();
+    const int v = pgemm::gemm_choose_variant(M, N, K, c);
+    const int64_t head = pgemm::gemm_head_rows(M, N, K, v, c);
     *head_rows = head;
     *head_variant = v;
     *tail_variant = head < M ? pgemm::gemm_small_partner(v) : 0;
