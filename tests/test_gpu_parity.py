@@ -539,6 +539,42 @@ def test_gemm_full_size_sampled(name, M, N, K, dist):
     assert_fp32_bound(got[I, J], ref, Sabs, K, name)
 
 
+def _random_auto_shapes(seed, n):
+    """Seeded ragged shapes across tile and wave boundaries (M any size;
+    N and K multiples of 8), at most 2e11 multiply-adds each."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.integers(0, 48)) * 128 + int(rng.choice([1, 8, 72, 128, 136]))
+        N = int(rng.integers(0, 48)) * 128 + int(rng.choice([8, 64, 120, 128]))
+        K = int(rng.choice([8, 56, 256, 1032, 4096, 8200]))
+        if M * N * K <= 2e11:
+            out.append((M, N, K))
+    return out
+
+
+def test_gemm_auto_random_shapes_sampled():
+    """The automatic path (the variant the tuned table and the fill rule
+    pick, and the row split) on random ragged shapes: every tile's corners,
+    four whole rows and columns and random outputs against the oracle."""
+    chosen = set()
+    for (M, N, K) in _random_auto_shapes(23, 30):
+        head, hv, tv = pg.pgemm_f16_plan(M, N, K, 0)
+        chosen.add(hv)
+        say("  auto %dx%dx%d: variant %d%s" % (M, N, K, hv,
+                                              " + %d rows on %d" % (M - head, tv) if tv else ""))
+        A, B = inputs.gemm_inputs(M, N, K, seed_a=M + 1, seed_b=N + 2)
+        C = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda:0")
+        got = host(pg.pgemm_f16(dev(A), dev(B), C=C))
+        I, J = inputs.sample_points(M, N, 1024, full_rows=4, full_cols=4, tile=128)
+        ref, _ = oracle.gemm_f16_points(A, B, I, J)
+        what = "auto %dx%dx%d" % (M, N, K)
+        assert_close(got[I, J], ref, what)
+        _, Sabs = oracle.gemm_f16_points(np.abs(A), np.abs(B), I, J)
+        assert_fp32_bound(got[I, J], ref, Sabs, K, what)
+    say("  variants chosen: %s" % sorted(chosen))
+
+
 def test_gemm_4096_every_output_vs_oracle():
     """The headline configuration (4096^3, U[-1,1]) on every one of its
     16,777,216 outputs: the whole result against the oracle, as the
