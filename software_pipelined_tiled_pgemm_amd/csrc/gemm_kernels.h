@@ -16,10 +16,11 @@
 //  * copy_start early / copy_wait late with several buffers (Pallas
 //    software-pipelining guide, section 4; max_concurrent_steps of the
 //    quickstart's emit_pipeline).  Two pipelines are implemented:
-//      - LDS-DMA pipeline (variants 1, 2, 5, 7, 8, and 9, its persistent
-//        form): a ring of 5 LDS stages of BK = 32.  copy_start is a
-//        buffer_load ... lds (global memory straight into LDS, no
-//        registers), issued 2 to 4 steps ahead and spread over the MFMA
+//      - LDS-DMA pipeline (variants 1, 2, 5, 7, 8, 9 -- the persistent
+//        form of 8 -- and 10, 11): a ring of 5 LDS stages of BK = 32 (7 or
+//        9 in variants 10 and 11).  copy_start is a buffer_load ... lds
+//        (global memory straight into LDS, no registers), issued up to S-1
+//        steps ahead for a ring of S stages and spread over the MFMA
 //        slots; copy_wait is an s_waitcnt on this wave's own copies followed
 //        by the workgroup barrier.
 //      - register-staged pipeline (variants 3, 4): 2 LDS stages of BK = 64
@@ -38,7 +39,7 @@
 //
 // Matrix instructions: v_mfma_f32_32x32x16_f16 (variants 1-6: 32x32 output
 // block, 16-deep K, 8 fp16 per lane per operand; lanes 0-31 carry K 0..7,
-// lanes 32-63 K 8..15) and v_mfma_f32_16x16x32_f16 (variants 7-9: 16x16
+// lanes 32-63 K 8..15) and v_mfma_f32_16x16x32_f16 (variants 7-11: 16x16
 // block, the whole K 32 of a stage; see Compute<TL, 16>).  Each MFMA computes
 // the transposed block C^T = B^T A^T (B^T as the row operand), so that each
 // lane ends up holding four consecutive columns of one row of C -- 8
