@@ -575,6 +575,31 @@ def test_gemm_auto_random_shapes_sampled():
     say("  variants chosen: %s" % sorted(chosen))
 
 
+def test_gemm_every_variant_at_4096_families_bit_identical():
+    """All variants at the headline size: bit-identical inside each
+    matrix-instruction family (the same K grouping at 256 tiles of 256x256
+    or 1024 of 128x128, one or two workgroups per CU, persistent or not,
+    5-, 7- or 9-slot rings), and each family within the bounds on the
+    full-size sample."""
+    M = N = K = 4096
+    A, B = inputs.gemm_inputs(M, N, K)
+    tA, tB = dev(A), dev(B)
+    I, J = inputs.sample_points(M, N, 8192)
+    ref, _ = oracle.gemm_f16_points(A, B, I, J)
+    _, Sabs = oracle.gemm_f16_points(np.abs(A), np.abs(B), I, J)
+    for fam in FAMILIES:
+        first = None
+        for v in fam:
+            C = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda:0")
+            got = gemm(tA, tB, v, C=C)
+            if first is None:
+                first = got
+                assert_close(got[I, J], ref, "variant %d at 4096^3" % v)
+                assert_fp32_bound(got[I, J], ref, Sabs, K, "variant %d at 4096^3" % v)
+            else:
+                assert bits_equal(got, first), "variant %d differs from variant %d at 4096^3" % (v, fam[0])
+
+
 def test_gemm_4096_every_output_vs_oracle():
     """The headline configuration (4096^3, U[-1,1]) on every one of its
     16,777,216 outputs: the whole result against the oracle, as the
