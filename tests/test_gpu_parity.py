@@ -314,6 +314,13 @@ SMALL_SHAPES = [
     (264, 136, 416),   # 13 steps: no unrolled pass, odd step count
     (256, 256, 480),   # 15 steps
     (128, 384, 832),   # 26 steps: two unrolled passes, a run-time one, tail
+    # the same boundaries of the 7- and 9-slot rings (variants 10, 11: a
+    # pass unrolls 2S steps and needs K/32 >= 3S - 1 steps)
+    (264, 136, 608),   # 19 steps: S = 7 runs no unrolled pass
+    (136, 264, 640),   # 20 steps: S = 7 one unrolled pass
+    (200, 200, 800),   # 25 steps: S = 9 no unrolled pass
+    (128, 256, 1184),  # 37 steps: S = 7 two passes, S = 9 one
+    (72, 136, 192),    # 6 steps = S - 1 for S = 7: the steady-state prologue
     # extreme aspect ratios: one row, the narrowest C, one tile row/column
     # with long K
     (1, 8192, 4096),
