@@ -186,10 +186,9 @@ int pgemm_f16_splitk_default_splits(int64_t M, int64_t N, int64_t K);
  * tile area) with slots = (workgroups per CU) * CUs and waves =
  * ceil(tiles / slots) for the variant's 256x256 or 128x128 tile, and the
  * best estimate (the lowest id within 1% of it) replaces T's variant if it
- * beats that variant's estimate by more than 30%.  Host
- * function: its only HIP calls read the current device's CU count, once per
- * device (256 when there is no device).  Returns PGEMM_EINVAL for a
- * negative size.
+ * beats that variant's estimate by more than 30%.  Host function: its only
+ * HIP calls read the current device's CU count, once per device (256 when
+ * there is no device).  Returns PGEMM_EINVAL for a negative size.
  */
 int pgemm_f16_choose_variant(int64_t M, int64_t N, int64_t K);
 
@@ -197,8 +196,9 @@ int pgemm_f16_choose_variant(int64_t M, int64_t N, int64_t K);
  * The launches pgemm_f16 makes for an M x N x K problem on a device with
  * `cus` compute units (cus <= 0: the current device's count, 256 if it
  * cannot be read).  Usually one: the variant pgemm_f16_choose_variant picks
- * on such a device, over all M rows (*head_rows = M, *tail_variant = 0).  When that variant uses
- * 256x256 tiles and their last wave over the CUs would be mostly idle, the
+ * on such a device, over all M rows (*head_rows = M, *tail_variant = 0).
+ * When that variant uses 256x256 tiles and their last wave over the CUs
+ * would be mostly idle, the
  * first *head_rows rows (a multiple of 256) run with it and the remaining
  * M - *head_rows rows with *tail_variant, the 128x128 variant of the same
  * matrix instruction, which gives bit-identical results.  The split minimises
@@ -207,9 +207,8 @@ int pgemm_f16_choose_variant(int64_t M, int64_t N, int64_t K);
  * only if it models at least 5% faster, for M*N*K of 1e10 or more.  Host
  * function: with cus > 0 it makes no HIP call; with cus <= 0 its only HIP
  * calls read the current device's attribute.  head_rows, head_variant,
- * tail_variant: host pointers,
- * written on success.  Returns PGEMM_EINVAL for a negative size or a null
- * pointer, else PGEMM_OK.
+ * tail_variant: host pointers, written on success.  Returns PGEMM_EINVAL for
+ * a negative size or a null pointer, else PGEMM_OK.
  */
 int pgemm_f16_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t* head_rows,
                    int* head_variant, int* tail_variant);

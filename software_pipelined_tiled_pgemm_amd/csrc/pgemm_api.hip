@@ -240,6 +240,6 @@ const char* pgemm_status_string(int status) {
 
 int pgemm_last_hip_error(void) { return g_last_hip_error; }
 
-int pgemm_version(void) { return 100; }
+int pgemm_version(void) { return 200; }
 
 }  // extern "C"
