@@ -905,7 +905,8 @@ def test_graph_capture_and_replay():
     # no synchronisation, no memset), so a captured sequence replays.  Each
     # replay follows eager work that poisons the outputs and is checked
     # against the eager results.
-    say("graph capture: gemm (auto, row split), split-K, stream add, x + c, reduction")
+    say("graph capture: gemm (auto, row split; persistent; 9-slot ring), split-K, stream add, "
+        "x + c, reduction")
     A, B = inputs.gemm_inputs(4392, 4352, 4096)
     tA, tB = dev(A), dev(B)
     A2, B2 = inputs.gemm_inputs(256, 264, 8192, seed_a=60, seed_b=61)
@@ -915,6 +916,8 @@ def test_graph_capture_and_replay():
     r = dev(inputs.uniform_f32((6, 1 << 18), 64))
     C = torch.empty((4392, 4352), dtype=torch.float16, device="cuda:0")
     C2 = torch.empty((256, 264), dtype=torch.float16, device="cuda:0")
+    C9 = torch.empty((4392, 4352), dtype=torch.float16, device="cuda:0")
+    C11 = torch.empty((256, 264), dtype=torch.float16, device="cuda:0")
     W = torch.empty(pg.pgemm_f16_splitk_workspace_bytes(256, 264, 8192, 4) // 4, device="cuda:0")
     z = torch.empty_like(tx)
     z1 = torch.empty_like(tx)
@@ -922,12 +925,14 @@ def test_graph_capture_and_replay():
 
     def work():
         pg.pgemm_f16(tA, tB, C=C)
+        pg.pgemm_f16_variant(tA, tB, 9, C=C9)
+        pg.pgemm_f16_variant(tA2, tB2, 11, C=C11)
         pg.pgemm_f16_splitk(tA2, tB2, 4, C=C2, workspace=W)
         pg.pstream_add(tx, ty, z=z)
         pg.pstream_add_scalar(tx, 1.0, z=z1)
         pg.preduce_sum_f32(r, out=o)
 
-    outs = (C, C2, z, z1, o)
+    outs = (C, C2, z, z1, o, C9, C11)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -945,3 +950,5 @@ def test_graph_capture_and_replay():
         for t, e in zip(outs, eager):
             assert bits_equal(host(t), e), "replay %d" % rep
     assert bits_equal(eager[2], oracle.add_f32(x, y))
+    # the persistent variant gives the automatic path's bits (same family)
+    assert bits_equal(eager[5], eager[0])
